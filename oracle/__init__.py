@@ -1,0 +1,135 @@
+"""fp64 CPU oracle for exact softmax attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never calls it, and the
+two share no code: the oracle is plain C (``oracle.c``) compiled with gcc.
+
+Functions take and return numpy float64 arrays laid out ``[BH, N, d]``
+(``[BH, N]`` for the logsumexp and D), C-contiguous.
+
+* :func:`attn_fwd` -- the plain definition of softmax attention (per head,
+  P = softmax(scale Q K^T), O = P V, L = natural-log logsumexp of the scaled
+  scores), as on the "FlashAttention" deep-dive page, section "How it works".
+* :func:`attn_bwd` -- its analytic gradients (same page and section: D =
+  rowsum(dO * O), dS = P * (dP - D), then dQ, dK, dV).
+* :func:`attn_fwd_tiled` -- the per-query-block online-softmax loop of that
+  page with deferred normalisation, used only to show tiled == untiled; it can
+  trace the running (m, l, acc) of one row, which the worked example on the
+  "Flash Attention and Memory-Efficient Attention Variants" page prints.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def build(force: bool = True) -> str:
+    """Compile ``liboracle.so`` with gcc (plain C11, -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared",
+             "-o", tmp, _SRC, "-lm", "-lpthread"],
+            check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_attn_fwd.argtypes = [_f64p] * 5 + [_i64, _i64, _i64, ctypes.c_double,
+                                                      ctypes.c_int, ctypes.c_int]
+        lib.oracle_attn_bwd.argtypes = [_f64p] * 8 + [_i64, _i64, _i64, ctypes.c_double,
+                                                      ctypes.c_int, ctypes.c_int]
+        lib.oracle_attn_fwd_tiled.argtypes = [_f64p] * 5 + [_i64, _i64, _i64, ctypes.c_double,
+                                                            ctypes.c_int, _i64, _i64, _i64, _f64p]
+        lib.oracle_default_threads.argtypes = []
+        for fn in (lib.oracle_attn_fwd, lib.oracle_attn_bwd, lib.oracle_attn_fwd_tiled,
+                   lib.oracle_default_threads):
+            fn.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    return int(_load().oracle_default_threads())
+
+
+def _as3(x, name):
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    if a.ndim == 2:
+        a = a[None]
+    if a.ndim != 3:
+        raise ValueError(f"{name} must be [BH, N, d] or [N, d]")
+    return a
+
+
+def _ptr(a):
+    return a.ctypes.data_as(_f64p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"{what} failed with code {rc}")
+
+
+def attn_fwd(q, k, v, scale, causal=False, threads=0):
+    """Returns (O [BH,N,d], L [BH,N]) in fp64."""
+    q, k, v = _as3(q, "q"), _as3(k, "k"), _as3(v, "v")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must have one shape")
+    BH, N, d = q.shape
+    o = np.empty_like(q)
+    lse = np.empty((BH, N), dtype=np.float64)
+    _check(_load().oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), BH, N, d,
+                                   float(scale), int(bool(causal)), int(threads)), "oracle_attn_fwd")
+    return o, lse
+
+
+def attn_bwd(q, k, v, dout, scale, causal=False, threads=0):
+    """Returns (dQ, dK, dV, D) in fp64, where D = rowsum(dO * O) with the
+    oracle's own O."""
+    q, k, v, dout = (_as3(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")))
+    if not (q.shape == k.shape == v.shape == dout.shape):
+        raise ValueError("q, k, v, dout must have one shape")
+    BH, N, d = q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    delta = np.empty((BH, N), dtype=np.float64)
+    _check(_load().oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                                   _ptr(dv), _ptr(delta), BH, N, d, float(scale),
+                                   int(bool(causal)), int(threads)), "oracle_attn_bwd")
+    return dq, dk, dv, delta
+
+
+def attn_fwd_tiled(q, k, v, scale, causal=False, br=64, bc=64, trace_row=None):
+    """Tiled online-softmax forward.  Returns (O, L) or, when ``trace_row`` is
+    given, (O, L, trace) with trace[blk] = [m, l, acc_0 .. acc_{d-1}] of that
+    row of head 0 after key block ``blk``."""
+    q, k, v = _as3(q, "q"), _as3(k, "k"), _as3(v, "v")
+    BH, N, d = q.shape
+    o = np.empty_like(q)
+    lse = np.empty((BH, N), dtype=np.float64)
+    nblk = -(-N // int(bc))
+    trace = np.full((nblk, 2 + d), np.nan) if trace_row is not None else None
+    _check(_load().oracle_attn_fwd_tiled(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), BH, N, d, float(scale),
+        int(bool(causal)), int(br), int(bc), -1 if trace_row is None else int(trace_row),
+        _ptr(trace) if trace is not None else None), "oracle_attn_fwd_tiled")
+    return (o, lse) if trace is None else (o, lse, trace)

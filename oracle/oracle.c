@@ -1,0 +1,367 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for exact softmax attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  The GPU path never calls it
+ * and shares no code with it.
+ *
+ * What it computes is the plain definition that FlashAttention reproduces
+ * exactly (the pages state the tiled kernel returns "exactly the same result"
+ * as standard attention; "FlashAttention Explained", section "Online
+ * softmax"; "Flash Attention and Memory-Efficient Attention Variants",
+ * worked example).  Per head, with S = scale * Q K^T:
+ *
+ *   P   = softmax(S) row-wise, over visible keys only
+ *   O   = P V
+ *   L_i = m_i + ln(sum_j exp(S_ij - m_i))        (natural-log logsumexp)
+ *
+ * The backward is the analytic derivative of O with respect to Q, K, V as
+ * outlined on the "FlashAttention" deep-dive page (section "How it works":
+ * D = rowsum(dO * O), dS = P * (dP - D)):
+ *
+ *   dV = P^T dO,   dP = dO V^T,   D_i = sum_t dO_it O_it,
+ *   dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
+ *
+ * A second forward, oracle_attn_fwd_tiled, follows the per-query-block loop of
+ * the same deep-dive page ("How it works": running row max m, running sum l,
+ * rescale alpha = exp(m - m_new), deferred division by l) in fp64, so that
+ * "tiled equals untiled" can be checked.  It also records the running state
+ * of one chosen row after every key block, which the worked example on the
+ * "Flash Attention and Memory-Efficient Attention Variants" page prints.
+ *
+ * Layout: every tensor is row-major contiguous [BH, N, d] (lse/delta [BH, N]),
+ * fp64.  Causal means key j is visible to query i iff j <= i (square,
+ * top-left aligned).  A row with no visible key (unreachable for square
+ * causal masks) gets O = 0 and L = -inf, as the deep-dive page's pitfalls
+ * section prescribes for fully masked rows.
+ *
+ * Parallelism: rows (forward, dQ) or keys (dK, dV) are split over POSIX
+ * threads; every output element is computed by exactly one thread in a fixed
+ * order, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_NOMEM 2
+
+static int resolve_threads(int nthreads) {
+    if (nthreads > 0) return nthreads;
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    return n > 0 ? (int)n : 1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A tiny "parallel for" over [0, count).                                   */
+
+typedef void (*range_fn)(void* ctx, int64_t begin, int64_t end);
+
+typedef struct {
+    range_fn fn;
+    void* ctx;
+    int64_t begin, end;
+    int running; /* 1 if a thread was started for this range */
+} range_job;
+
+static void* range_thread(void* p) {
+    range_job* j = (range_job*)p;
+    j->fn(j->ctx, j->begin, j->end);
+    return NULL;
+}
+
+static int parallel_for(int64_t count, int nthreads, range_fn fn, void* ctx) {
+    int nt = resolve_threads(nthreads);
+    if ((int64_t)nt > count) nt = (int)(count > 0 ? count : 1);
+    if (nt <= 1) {
+        fn(ctx, 0, count);
+        return ORACLE_OK;
+    }
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+    range_job* jobs = (range_job*)malloc(sizeof(range_job) * (size_t)nt);
+    if (!th || !jobs) {
+        free(th);
+        free(jobs);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (int t = 0; t < nt; ++t) {
+        jobs[t].fn = fn;
+        jobs[t].ctx = ctx;
+        jobs[t].begin = count * t / nt;
+        jobs[t].end = count * (t + 1) / nt;
+        jobs[t].running = pthread_create(&th[t], NULL, range_thread, &jobs[t]) == 0;
+        if (!jobs[t].running) fn(ctx, jobs[t].begin, jobs[t].end); /* no thread: do it here */
+    }
+    for (int t = 0; t < nt; ++t)
+        if (jobs[t].running) pthread_join(th[t], NULL);
+    free(th);
+    free(jobs);
+    return ORACLE_OK;
+}
+
+static int visible(int causal, int64_t i, int64_t j) { return !causal || j <= i; }
+
+/* ------------------------------------------------------------------------ */
+/* Forward: the plain definition, one query row at a time.                   */
+
+typedef struct {
+    const double *q, *k, *v;
+    double *o, *lse;
+    int64_t N, d;
+    double scale;
+    int causal;
+} fwd_ctx;
+
+static void fwd_rows(void* p, int64_t begin, int64_t end) {
+    fwd_ctx* c = (fwd_ctx*)p;
+    const int64_t N = c->N, d = c->d;
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    for (int64_t r = begin; r < end; ++r) { /* r = bh * N + i */
+        const int64_t bh = r / N, i = r % N;
+        const double* qi = c->q + r * d;
+        const double* kh = c->k + bh * N * d;
+        const double* vh = c->v + bh * N * d;
+        double* oi = c->o + r * d;
+        /* scores of the visible keys, and their maximum */
+        double m = -INFINITY;
+        for (int64_t j = 0; j < N; ++j) {
+            if (!visible(c->causal, i, j)) continue;
+            double dot = 0.0;
+            for (int64_t t = 0; t < d; ++t) dot += qi[t] * kh[j * d + t];
+            s[j] = c->scale * dot;
+            if (s[j] > m) m = s[j];
+        }
+        for (int64_t t = 0; t < d; ++t) oi[t] = 0.0;
+        if (m == -INFINITY) { /* no visible key: O = 0, L = -inf */
+            c->lse[r] = -INFINITY;
+            continue;
+        }
+        /* softmax denominator, then O = sum_j softmax_j * v_j */
+        double l = 0.0;
+        for (int64_t j = 0; j < N; ++j)
+            if (visible(c->causal, i, j)) l += exp(s[j] - m);
+        for (int64_t j = 0; j < N; ++j) {
+            if (!visible(c->causal, i, j)) continue;
+            const double pij = exp(s[j] - m) / l;
+            for (int64_t t = 0; t < d; ++t) oi[t] += pij * vh[j * d + t];
+        }
+        c->lse[r] = m + log(l);
+    }
+    free(s);
+}
+
+int oracle_attn_fwd(const double* q, const double* k, const double* v, double* o, double* lse,
+                    int64_t BH, int64_t N, int64_t d, double scale, int causal, int nthreads) {
+    if (!q || !k || !v || !o || !lse || BH <= 0 || N <= 0 || d <= 0) return ORACLE_ERR_ARG;
+    fwd_ctx c = {q, k, v, o, lse, N, d, scale, causal};
+    return parallel_for(BH * N, nthreads, fwd_rows, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward: analytic gradients with the full N x N matrices of each head.   */
+
+typedef struct {
+    const double *q, *k, *v, *dout;
+    double *dq, *dk, *dv, *delta;
+    double *P, *dS; /* N x N scratch of the current head */
+    double *o, *lse; /* this head's forward outputs */
+    int64_t N, d;
+    double scale;
+    int causal;
+} bwd_ctx;
+
+/* rows i: P_i, O_i, L_i, D_i, dS_i and dQ_i */
+static void bwd_rows(void* p, int64_t begin, int64_t end) {
+    bwd_ctx* c = (bwd_ctx*)p;
+    const int64_t N = c->N, d = c->d;
+    for (int64_t i = begin; i < end; ++i) {
+        const double* qi = c->q + i * d;
+        double* Pi = c->P + i * N;
+        double* dSi = c->dS + i * N;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < N; ++j) {
+            Pi[j] = -INFINITY;
+            if (!visible(c->causal, i, j)) continue;
+            double dot = 0.0;
+            for (int64_t t = 0; t < d; ++t) dot += qi[t] * c->k[j * d + t];
+            Pi[j] = c->scale * dot; /* holds S_ij for now */
+            if (Pi[j] > m) m = Pi[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < N; ++j)
+            if (visible(c->causal, i, j)) l += exp(Pi[j] - m);
+        for (int64_t j = 0; j < N; ++j)
+            Pi[j] = (m == -INFINITY || !visible(c->causal, i, j)) ? 0.0 : exp(Pi[j] - m) / l;
+        c->lse[i] = (m == -INFINITY) ? -INFINITY : m + log(l);
+        /* O_i = P_i V and D_i = dO_i . O_i */
+        double* oi = c->o + i * d;
+        for (int64_t t = 0; t < d; ++t) oi[t] = 0.0;
+        for (int64_t j = 0; j < N; ++j)
+            for (int64_t t = 0; t < d; ++t) oi[t] += Pi[j] * c->v[j * d + t];
+        const double* doi = c->dout + i * d;
+        double Di = 0.0;
+        for (int64_t t = 0; t < d; ++t) Di += doi[t] * oi[t];
+        c->delta[i] = Di;
+        /* dP_ij = dO_i . v_j ; dS_ij = P_ij (dP_ij - D_i) ; dQ_i = scale sum_j dS_ij k_j */
+        double* dqi = c->dq + i * d;
+        for (int64_t t = 0; t < d; ++t) dqi[t] = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            double dP = 0.0;
+            for (int64_t t = 0; t < d; ++t) dP += doi[t] * c->v[j * d + t];
+            dSi[j] = Pi[j] * (dP - Di);
+            for (int64_t t = 0; t < d; ++t) dqi[t] += dSi[j] * c->k[j * d + t];
+        }
+        for (int64_t t = 0; t < d; ++t) dqi[t] *= c->scale;
+    }
+}
+
+/* columns j: dV_j = sum_i P_ij dO_i ; dK_j = scale sum_i dS_ij q_i */
+static void bwd_cols(void* p, int64_t begin, int64_t end) {
+    bwd_ctx* c = (bwd_ctx*)p;
+    const int64_t N = c->N, d = c->d;
+    for (int64_t j = begin; j < end; ++j) {
+        double* dvj = c->dv + j * d;
+        double* dkj = c->dk + j * d;
+        for (int64_t t = 0; t < d; ++t) dvj[t] = dkj[t] = 0.0;
+        for (int64_t i = 0; i < N; ++i) {
+            const double Pij = c->P[i * N + j], dSij = c->dS[i * N + j];
+            for (int64_t t = 0; t < d; ++t) {
+                dvj[t] += Pij * c->dout[i * d + t];
+                dkj[t] += dSij * c->q[i * d + t];
+            }
+        }
+        for (int64_t t = 0; t < d; ++t) dkj[t] *= c->scale;
+    }
+}
+
+/* delta may be NULL; otherwise it receives D = rowsum(dO * O) with the
+ * oracle's own fp64 O. */
+int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
+                    double* dq, double* dk, double* dv, double* delta,
+                    int64_t BH, int64_t N, int64_t d, double scale, int causal, int nthreads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || BH <= 0 || N <= 0 || d <= 0)
+        return ORACLE_ERR_ARG;
+    double* P = (double*)malloc(sizeof(double) * (size_t)(N * N));
+    double* dS = (double*)malloc(sizeof(double) * (size_t)(N * N));
+    double* o = (double*)malloc(sizeof(double) * (size_t)(N * d));
+    double* lse = (double*)malloc(sizeof(double) * (size_t)N);
+    double* dl = (double*)malloc(sizeof(double) * (size_t)N);
+    int rc = ORACLE_OK;
+    if (!P || !dS || !o || !lse || !dl) rc = ORACLE_ERR_NOMEM;
+    for (int64_t bh = 0; bh < BH && rc == ORACLE_OK; ++bh) {
+        const int64_t off = bh * N * d;
+        bwd_ctx c = {q + off, k + off, v + off, dout + off, dq + off, dk + off, dv + off, dl,
+                     P, dS, o, lse, N, d, scale, causal};
+        rc = parallel_for(N, nthreads, bwd_rows, &c);
+        if (rc == ORACLE_OK) rc = parallel_for(N, nthreads, bwd_cols, &c);
+        if (delta) memcpy(delta + bh * N, dl, sizeof(double) * (size_t)N);
+    }
+    free(P);
+    free(dS);
+    free(o);
+    free(lse);
+    free(dl);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Tiled forward with online softmax (deferred normalisation), in fp64.      */
+/*                                                                           */
+/* For each block of br query rows: m = -inf, l = 0, acc = 0; for each block */
+/* of bc keys: S = scale Q_i K_j^T (masked keys -> -inf), m_new = max(m,     */
+/* rowmax S), P = exp(S - m_new), alpha = exp(m - m_new) (0 while m = -inf),  */
+/* l = alpha l + rowsum P, acc = alpha acc + P V_j, m = m_new.  Finally       */
+/* O = acc / l and L = m + ln l.                                              */
+/*                                                                           */
+/* trace (may be NULL) receives, for the query row trace_row of head 0, one  */
+/* record of 2 + d doubles per key block: m, l, acc[0..d-1].  It must hold   */
+/* ceil(N / bc) records.                                                      */
+
+int oracle_attn_fwd_tiled(const double* q, const double* k, const double* v, double* o, double* lse,
+                          int64_t BH, int64_t N, int64_t d, double scale, int causal,
+                          int64_t br, int64_t bc, int64_t trace_row, double* trace) {
+    if (!q || !k || !v || !o || !lse || BH <= 0 || N <= 0 || d <= 0 || br <= 0 || bc <= 0)
+        return ORACLE_ERR_ARG;
+    double* S = (double*)malloc(sizeof(double) * (size_t)(br * bc));
+    double* m = (double*)malloc(sizeof(double) * (size_t)br);
+    double* l = (double*)malloc(sizeof(double) * (size_t)br);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)(br * d));
+    if (!S || !m || !l || !acc) {
+        free(S);
+        free(m);
+        free(l);
+        free(acc);
+        return ORACLE_ERR_NOMEM;
+    }
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const double* qh = q + bh * N * d;
+        const double* kh = k + bh * N * d;
+        const double* vh = v + bh * N * d;
+        for (int64_t i0 = 0; i0 < N; i0 += br) {
+            const int64_t rows = (N - i0 < br) ? N - i0 : br;
+            for (int64_t r = 0; r < rows; ++r) {
+                m[r] = -INFINITY;
+                l[r] = 0.0;
+                for (int64_t t = 0; t < d; ++t) acc[r * d + t] = 0.0;
+            }
+            for (int64_t j0 = 0, blk = 0; j0 < N; j0 += bc, ++blk) {
+                const int64_t cols = (N - j0 < bc) ? N - j0 : bc;
+                for (int64_t r = 0; r < rows; ++r) {
+                    const int64_t i = i0 + r;
+                    double rowmax = -INFINITY;
+                    for (int64_t cc = 0; cc < cols; ++cc) {
+                        const int64_t j = j0 + cc;
+                        double sv = -INFINITY;
+                        if (visible(causal, i, j)) {
+                            double dot = 0.0;
+                            for (int64_t t = 0; t < d; ++t) dot += qh[i * d + t] * kh[j * d + t];
+                            sv = scale * dot;
+                        }
+                        S[r * bc + cc] = sv;
+                        if (sv > rowmax) rowmax = sv;
+                    }
+                    const double m_new = m[r] > rowmax ? m[r] : rowmax;
+                    if (m_new != -INFINITY) { /* else: nothing visible yet */
+                        const double alpha = (m[r] == -INFINITY) ? 0.0 : exp(m[r] - m_new);
+                        double rowsum = 0.0;
+                        for (int64_t t = 0; t < d; ++t) acc[r * d + t] *= alpha;
+                        for (int64_t cc = 0; cc < cols; ++cc) {
+                            const double pv = exp(S[r * bc + cc] - m_new); /* exp(-inf) = 0 */
+                            rowsum += pv;
+                            for (int64_t t = 0; t < d; ++t) acc[r * d + t] += pv * vh[(j0 + cc) * d + t];
+                        }
+                        l[r] = alpha * l[r] + rowsum;
+                        m[r] = m_new;
+                    }
+                    if (trace && bh == 0 && i == trace_row) {
+                        double* rec = trace + blk * (2 + d);
+                        rec[0] = m[r];
+                        rec[1] = l[r];
+                        for (int64_t t = 0; t < d; ++t) rec[2 + t] = acc[r * d + t];
+                    }
+                }
+            }
+            for (int64_t r = 0; r < rows; ++r) {
+                double* oi = o + (bh * N + i0 + r) * d;
+                if (m[r] == -INFINITY) {
+                    for (int64_t t = 0; t < d; ++t) oi[t] = 0.0;
+                    lse[bh * N + i0 + r] = -INFINITY;
+                } else {
+                    for (int64_t t = 0; t < d; ++t) oi[t] = acc[r * d + t] / l[r];
+                    lse[bh * N + i0 + r] = m[r] + log(l[r]);
+                }
+            }
+        }
+    }
+    free(S);
+    free(m);
+    free(l);
+    free(acc);
+    return ORACLE_OK;
+}
+
+int oracle_default_threads(void) { return resolve_threads(0); }

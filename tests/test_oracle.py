@@ -1,0 +1,336 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+No GPU.  Every check compares the oracle with something other than itself:
+values printed on the pages (tests/golden), closed forms, invariants, special
+cases that reduce to library routines (scipy's softmax/logsumexp, torch's fp64
+autograd), brute-force finite differences, and the tiled formulation.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+from io_aware_tiled_fwd_amd import inputs
+
+
+
+def _worked(golden):
+    g = golden("worked_example.txt")
+    q = np.array(g["q"][0])
+    K = np.array([g[f"K{i}"][0] for i in range(4)])
+    V = np.array([g[f"V{i}"][0] for i in range(4)])
+    return g, q, K, V
+
+
+def _close(got, want_tol, what):
+    want, tol = want_tol
+    got = np.atleast_1d(np.asarray(got, dtype=np.float64))
+    assert got.shape == (len(want),), what
+    err = np.max(np.abs(got - np.array(want)))
+    assert err <= tol, f"{what}: got {got}, page prints {want} (tol {tol}, err {err})"
+
+
+# --- the worked example (page 5) ------------------------------------------------
+
+def test_worked_example_direct(golden):
+    """Plain oracle: the query row of the worked example gives the printed output."""
+    g, q, K, V = _worked(golden)
+    Q = np.zeros((4, 2))
+    Q[0] = q
+    Q[1:] = [[0.5, -1.0], [2.0, 0.25], [-0.75, 1.5]]  # other rows are independent
+    O, L = oracle.attn_fwd(Q, K, V, scale=g["scale"][0][0])
+    _close(O[0, 0], g["final_o_printed"], "O (printed program output)")
+    _close(O[0, 0], g["final_o_hand"], "O (hand trace)")
+    # L = m + ln l, m = 3 is the row max and l the softmax denominator (1.20344)
+    _close(np.exp(L[0, 0] - 3.0), g["tile2_l"], "exp(L - m)")
+    _close(np.exp(L[0, 0] - 3.0), g["block4_l"], "exp(L - m), one block")
+
+
+def test_worked_example_probabilities(golden):
+    """With V = identity the output row is the probability row."""
+    g, q, K, _ = _worked(golden)
+    Q = np.zeros((4, 4))
+    Q[0, :2] = q
+    K4 = np.zeros((4, 4))
+    K4[:, :2] = K
+    O, _ = oracle.attn_fwd(Q, K4, np.eye(4), scale=1.0)
+    _close(O[0, 0], g["probs"], "softmax probabilities")
+
+
+def test_worked_example_tile_trace(golden):
+    """Tiled oracle with key blocks of 2 reproduces the page's per-tile trace."""
+    g, q, K, V = _worked(golden)
+    Q = np.zeros((4, 2))
+    Q[0] = q
+    O, L, tr = oracle.attn_fwd_tiled(Q, K, V, scale=1.0, br=4, bc=2, trace_row=0)
+    assert tr.shape == (2, 4)
+    _close(tr[0, 0], g["tile1_m"], "m after tile 1")
+    _close(tr[0, 1], g["tile1_l"], "l after tile 1")
+    _close(tr[0, 2:], g["tile1_acc"], "acc after tile 1")
+    _close(tr[1, 0], g["tile2_m"], "m after tile 2")
+    _close(tr[1, 1], g["tile2_l"], "l after tile 2")
+    _close(tr[1, 2:], g["tile2_acc"], "acc after tile 2")
+    _close(np.exp(tr[0, 0] - tr[1, 0]), g["tile2_correction"], "rescale factor exp(m_old - m_new)")
+    _close(O[0, 0], g["final_o_printed"], "tiled O")
+    # one block of four keys: same l and O
+    O4, _, tr4 = oracle.attn_fwd_tiled(Q, K, V, scale=1.0, br=4, bc=4, trace_row=0)
+    assert tr4.shape == (1, 4)
+    _close(tr4[0, 1], g["block4_l"], "l with one block")
+    _close(O4[0, 0], g["final_o_printed"], "O with one block")
+
+
+def test_worked_example_unnormalised_p(golden):
+    """The page's per-tile p = exp(s - m_new) values follow from the scores it
+    prints and the trace's running max."""
+    g, q, K, V = _worked(golden)
+    s = K @ q
+    _close(s, g["scores"], "scores")
+    _, _, tr = oracle.attn_fwd_tiled(np.vstack([q, np.zeros((3, 2))]), K, V, 1.0, br=4, bc=2,
+                                     trace_row=0)
+    _close(np.exp(s[:2] - tr[0, 0]), g["tile1_p"], "tile 1 p")
+    _close(np.exp(s[2:] - tr[1, 0]), g["tile2_p"], "tile 2 p")
+    _close(np.exp(s - 3.0), g["block4_p"], "block-4 p")
+
+
+# --- the deep-dive page's self-test recipe (page 4) -----------------------------
+
+def test_page_recipe_tiled_vs_naive():
+    """n=300, d=64, the page's generator with seeds 1/2/3, 64x64 tiles (ragged):
+    tiled output within 1e-4 of naive attention, as the page asserts."""
+    n, d = 300, 64
+    q, k, v = (inputs.page_generator(n, d, s).astype(np.float64) for s in (1, 2, 3))
+    scale = 1.0 / math.sqrt(d)
+    O_t, L_t = oracle.attn_fwd_tiled(q, k, v, scale, br=64, bc=64)
+    O_n, L_n = oracle.attn_fwd(q, k, v, scale)
+    assert np.max(np.abs(O_t - O_n)) < 1e-4
+    assert np.max(np.abs(O_t - O_n)) < 1e-12  # both fp64
+    assert np.max(np.abs(L_t - L_n)) < 1e-12
+
+
+# --- library routines -------------------------------------------------------
+
+def _masked_scores(q, k, scale, causal):
+    S = scale * np.einsum("bid,bjd->bij", q, k)
+    if causal:
+        N = q.shape[1]
+        S = np.where(np.tril(np.ones((N, N), dtype=bool))[None], S, -np.inf)
+    return S
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_against_scipy_softmax(causal):
+    rng = np.random.default_rng(7)
+    BH, N, d = 3, 37, 16
+    q, k, v = (rng.standard_normal((BH, N, d)) * 1.7 for _ in range(3))
+    scale = 0.3
+    O, L = oracle.attn_fwd(q, k, v, scale, causal)
+    S = _masked_scores(q, k, scale, causal)
+    P = scipy.special.softmax(S, axis=-1)
+    np.testing.assert_allclose(O, P @ v, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(L, scipy.special.logsumexp(S, axis=-1), rtol=1e-13, atol=1e-13)
+
+
+def test_against_torch_sdpa_fp64():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    BH, N, d = 2, 29, 8
+    q, k, v = (rng.standard_normal((BH, N, d)) for _ in range(3))
+    for causal in (False, True):
+        O, _ = oracle.attn_fwd(q, k, v, 0.4, causal)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+            is_causal=causal, scale=0.4).numpy()
+        np.testing.assert_allclose(O, ref, rtol=1e-12, atol=1e-12)
+
+
+# --- closed forms and invariants -------------------------------------------
+
+def test_rows_of_p_sum_to_one():
+    rng = np.random.default_rng(3)
+    N = d = 24
+    q, k = rng.standard_normal((N, d)) * 2, rng.standard_normal((N, d)) * 2
+    for causal in (False, True):
+        P, _ = oracle.attn_fwd(q, k, np.eye(N), 1.0, causal)
+        assert np.all(P >= 0)
+        assert np.max(np.abs(P.sum(-1) - 1.0)) <= 1e-14 * N
+        if causal:
+            assert np.all(np.triu(P[0], 1) == 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v(causal):
+    rng = np.random.default_rng(5)
+    BH, N, d = 2, 50, 8
+    q, k = rng.standard_normal((BH, N, d)), rng.standard_normal((BH, N, d))
+    c = rng.standard_normal(d)
+    v = np.broadcast_to(c, (BH, N, d)).copy()
+    O, _ = oracle.attn_fwd(q, k, v, 0.5, causal)
+    np.testing.assert_allclose(O, v, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_q_zero(causal):
+    rng = np.random.default_rng(6)
+    BH, N, d = 2, 40, 8
+    k, v = rng.standard_normal((BH, N, d)), rng.standard_normal((BH, N, d))
+    O, L = oracle.attn_fwd(np.zeros((BH, N, d)), k, v, 0.7, causal)
+    if causal:
+        counts = np.arange(1, N + 1)[None, :, None]
+        np.testing.assert_allclose(O, np.cumsum(v, axis=1) / counts, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(L, np.log(np.arange(1, N + 1))[None].repeat(BH, 0), atol=1e-14)
+    else:
+        np.testing.assert_allclose(O, v.mean(axis=1, keepdims=True).repeat(N, 1), atol=1e-14)
+        np.testing.assert_allclose(L, np.full((BH, N), math.log(N)), atol=1e-14)
+
+
+def test_causal_row0():
+    rng = np.random.default_rng(8)
+    BH, N, d = 3, 20, 8
+    q, k, v = (rng.standard_normal((BH, N, d)) for _ in range(3))
+    O, L = oracle.attn_fwd(q, k, v, 0.35, True)
+    np.testing.assert_array_equal(O[:, 0], v[:, 0])
+    np.testing.assert_allclose(L[:, 0], 0.35 * np.sum(q[:, 0] * k[:, 0], -1), rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_invariance(causal):
+    """K' = K + 1 u^T leaves O unchanged and adds scale * q_i . u to L_i."""
+    rng = np.random.default_rng(9)
+    BH, N, d = 2, 31, 8
+    q, k, v = (rng.standard_normal((BH, N, d)) for _ in range(3))
+    u = rng.standard_normal(d)
+    O, L = oracle.attn_fwd(q, k, v, 0.6, causal)
+    O2, L2 = oracle.attn_fwd(q, k + u, v, 0.6, causal)
+    np.testing.assert_allclose(O2, O, atol=1e-12)
+    np.testing.assert_allclose(L2, L + 0.6 * (q @ u), atol=1e-12)
+
+
+def test_permutations():
+    rng = np.random.default_rng(10)
+    N, d = 33, 8
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    O, L = oracle.attn_fwd(q, k, v, 0.5)
+    pk = rng.permutation(N)
+    O2, L2 = oracle.attn_fwd(q, k[pk], v[pk], 0.5)
+    np.testing.assert_allclose(O2, O, atol=1e-13)
+    np.testing.assert_allclose(L2, L, atol=1e-13)
+    pq = rng.permutation(N)
+    O3, L3 = oracle.attn_fwd(q[pq], k, v, 0.5)
+    np.testing.assert_allclose(O3[0], O[0][pq], atol=1e-13)
+    np.testing.assert_allclose(L3[0], L[0][pq], atol=1e-13)
+
+
+def test_scale_enters_as_product_with_q():
+    rng = np.random.default_rng(12)
+    N, d = 21, 8
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    O, L = oracle.attn_fwd(q, k, v, 0.25)
+    O2, L2 = oracle.attn_fwd(q * 4.0, k, v, 0.0625)
+    np.testing.assert_allclose(O2, O, atol=1e-13)
+    np.testing.assert_allclose(L2, L, atol=1e-13)
+    # and scale does matter: a different scale changes the result
+    O3, _ = oracle.attn_fwd(q, k, v, 0.5)
+    assert np.max(np.abs(O3 - O)) > 1e-3
+
+
+@pytest.mark.parametrize("N", [1, 5, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiled_equals_untiled(N, causal):
+    rng = np.random.default_rng(N)
+    d = 16
+    q, k, v = (rng.standard_normal((2, N, d)) * 2 for _ in range(3))
+    O, L = oracle.attn_fwd(q, k, v, 0.25, causal)
+    for blk in (1, 2, 7, 64, N):
+        for br in (blk, 3):
+            Ot, Lt = oracle.attn_fwd_tiled(q, k, v, 0.25, causal, br=br, bc=blk)
+            assert np.max(np.abs(Ot - O)) <= 1e-12, (blk, br)
+            assert np.max(np.abs(Lt - L)) <= 1e-12, (blk, br)
+
+
+def test_thread_count_does_not_change_results():
+    rng = np.random.default_rng(13)
+    q, k, v, g = (rng.standard_normal((2, 45, 8)) for _ in range(4))
+    a = oracle.attn_fwd(q, k, v, 0.3, True, threads=1)
+    b = oracle.attn_fwd(q, k, v, 0.3, True, threads=7)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    a = oracle.attn_bwd(q, k, v, g, 0.3, True, threads=1)
+    b = oracle.attn_bwd(q, k, v, g, 0.3, True, threads=5)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+# --- backward -----------------------------------------------------------------
+
+def _fd_grads(q, k, v, g, scale, causal, h=1e-6):
+    """Central finite differences of f = sum(O * G) through the pinned forward."""
+    def f(q_, k_, v_):
+        return float(np.sum(oracle.attn_fwd(q_, k_, v_, scale, causal, threads=1)[0] * g))
+    out = []
+    for which in range(3):
+        base = [q, k, v]
+        grad = np.zeros_like(base[which])
+        for idx in np.ndindex(grad.shape):
+            plus = [x.copy() for x in base]
+            minus = [x.copy() for x in base]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            grad[idx] = (f(*plus) - f(*minus)) / (2 * h)
+        out.append(grad)
+    return out
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,d", [(1, 3), (4, 2), (6, 4)])
+def test_backward_finite_differences(causal, N, d):
+    rng = np.random.default_rng(100 + N)
+    q, k, v, g = (rng.standard_normal((1, N, d)) for _ in range(4))
+    dq, dk, dv, _ = oracle.attn_bwd(q, k, v, g, 0.7, causal)
+    for name, got, want in zip("qkv", (dq, dk, dv), _fd_grads(q, k, v, g, 0.7, causal)):
+        scale_ = max(1.0, np.max(np.abs(want)))
+        assert np.max(np.abs(got - want)) <= 1e-7 * scale_, name
+
+
+def test_backward_against_torch_autograd_fp64():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    BH, N, d = 2, 17, 8
+    arrs = [rng.standard_normal((BH, N, d)) for _ in range(4)]
+    for causal in (False, True):
+        dq, dk, dv, _ = oracle.attn_bwd(*arrs, 0.45, causal)
+        tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in arrs[:3])
+        S = 0.45 * tq @ tk.transpose(-1, -2)
+        if causal:
+            S = S.masked_fill(~torch.ones(N, N, dtype=torch.bool).tril(), float("-inf"))
+        O = torch.softmax(S, -1) @ tv
+        O.backward(torch.tensor(arrs[3]))
+        for got, t in zip((dq, dk, dv), (tq, tk, tv)):
+            np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    """sum_j dS_ij = 0 gives sum_j dK_j = 0; sum_i P_ij summed over j gives
+    sum_j dV_j = sum_i dO_i; D equals rowsum(dO * O) of the forward."""
+    rng = np.random.default_rng(22)
+    BH, N, d = 2, 64, 16
+    q, k, v, g = (rng.standard_normal((BH, N, d)) for _ in range(4))
+    dq, dk, dv, D = oracle.attn_bwd(q, k, v, g, 0.25, causal)
+    np.testing.assert_allclose(dk.sum(1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(dv.sum(1), g.sum(1), atol=1e-12)
+    O, _ = oracle.attn_fwd(q, k, v, 0.25, causal)
+    np.testing.assert_allclose(D, np.sum(g * O, -1), atol=1e-13)
+
+
+def test_causal_backward_last_key_row0():
+    """Under a causal mask, query 0 sees only key 0, and the last key is seen
+    only by the last query: dV_{N-1} = P_{N-1,N-1} dO_{N-1}."""
+    rng = np.random.default_rng(23)
+    N, d = 9, 4
+    q, k, v, g = (rng.standard_normal((1, N, d)) for _ in range(4))
+    _, dk, dv, _ = oracle.attn_bwd(q, k, v, g, 0.5, True)
+    S = 0.5 * q[0] @ k[0].T
+    p_last = math.exp(S[N - 1, N - 1] - scipy.special.logsumexp(S[N - 1]))
+    np.testing.assert_allclose(dv[0, N - 1], p_last * g[0, N - 1], atol=1e-14)
