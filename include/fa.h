@@ -1,0 +1,101 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact tiled attention (FlashAttention forward and
+ * backward) on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is softmax attention per (batch, head):
+ *
+ *   S = scale * Q K^T,  P = softmax(S) row-wise,  O = P V,
+ *   L_i = logsumexp_j S_ij  (natural log),
+ *
+ * computed tile by tile with an online softmax so that S and P never reach
+ * HBM; only O and the per-row logsumexp L are written.  The interface and
+ * outputs follow the "FlashAttention" deep-dive page (tirogla.com), section
+ * "How it works": in Q, K, V of shape N x d per head; out O and one
+ * logsumexp per row; no state between calls.  The backward recomputes P from
+ * L and forms dQ, dK, dV from D = rowsum(dO * O) and dS = P * (dP - D) (same
+ * section).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers into memory the caller owns.  The
+ *    library allocates nothing, keeps no state between calls and may be called
+ *    concurrently on different streams.
+ *  - Layout: row-major contiguous [B, H, N, d] for q, k, v, o, dO, dq, dk, dv;
+ *    [B, H, N] for lse and delta.  Base pointers must be 16-byte aligned.
+ *    Outputs must not alias inputs.
+ *  - bf16 means IEEE-754 binary32 truncated to its upper 16 bits (bfloat16);
+ *    bf16 outputs are rounded to nearest, ties to even.
+ *  - causal != 0 applies the square, top-left aligned mask: key j is visible to
+ *    query i iff j <= i.  Tiles entirely above the diagonal are skipped.
+ *  - scale is any finite float; callers usually pass 1/sqrt(d).
+ *  - lse is the natural-log logsumexp of the SCALED scores (the value that the
+ *    deep-dive page's pseudocode stores as L = m + log l).
+ *  - Calls are asynchronous on `stream` (0 = the null stream); outputs are
+ *    valid once the stream reaches the call.  The host never synchronises.
+ *  - Arguments are validated before any launch; on an error nothing is
+ *    launched and outputs are untouched.  No exception crosses the ABI.
+ *
+ * Supported shapes: B, H, N >= 1 with B*H <= 2^31-1 and B*H*N*d < 2^62
+ * (element offsets are 64-bit), d in {64, 128}.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1, /* null pointer, B/H/N < 1, non-finite scale, size overflow */
+    FA_ERR_UNSUPPORTED = 2, /* head dimension d not in {64, 128} */
+    FA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} fa_status;
+
+/*
+ * Forward, bf16 inputs and output, fp32 arithmetic.
+ *   q, k, v : const bf16 [B,H,N,d]
+ *   o       : bf16 [B,H,N,d]      attention output, O = softmax(scale Q K^T) V
+ *   lse     : float [B,H,N]       natural-log logsumexp of each scaled score row
+ * S, the running row max/sum and the output accumulator are fp32; P is rounded
+ * to bf16 only as the operand of the P V product (deep-dive page,
+ * "Implementation notes").
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Forward, fp32 inputs and output.  Same semantics as fa_fwd; every product
+ * and sum is fp32 (P is not rounded to bf16).
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Backward, bf16 inputs, fp32 gradients.
+ *   q, k, v : const bf16 [B,H,N,d]  the forward's inputs
+ *   o       : const bf16 [B,H,N,d]  the forward's output
+ *   lse     : const float [B,H,N]   the forward's logsumexp (natural log)
+ *   dO      : const bf16 [B,H,N,d]  gradient of the loss with respect to o
+ *   dq, dk, dv : float [B,H,N,d]    gradients with respect to q, k, v (written,
+ *                                   not accumulated into)
+ *   delta   : float [B,H,N]         caller-provided workspace; receives
+ *                                   D_i = sum_t dO_it * O_it
+ * P is recomputed tile by tile as exp(scale q_i.k_j - L_i); dS = P * (dP - D);
+ * dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.  dQ is accumulated by one
+ * workgroup per query block (no atomics), so results are bitwise reproducible.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dO, float* dq, float* dk, float* dv, float* delta,
+           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

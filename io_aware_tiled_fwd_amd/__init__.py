@@ -1,0 +1,19 @@
+"""Exact tiled attention (FlashAttention forward and backward) for MI355X.
+
+The computation lives in ``libfa.so`` (hand-written gfx950 HIP kernels behind
+the C ABI in ``include/fa.h``); :mod:`io_aware_tiled_fwd_amd.binding` is a thin
+ctypes layer over it.  Importing this package does not load the library;
+the first call does, and fails loudly if it has not been built
+(``python -m io_aware_tiled_fwd_amd.build``).
+"""
+_BINDING_NAMES = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_status_string", "attention_fwd",
+                  "attention_bwd", "FaError", "load_library")
+
+__all__ = list(_BINDING_NAMES)
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,170 @@
+"""Thin ctypes binding of libfa.so (include/fa.h).
+
+Argument marshalling only: shapes, dtypes and devices of torch tensors are
+checked, raw device pointers and the current HIP stream are passed to the C
+entry points, and a non-zero status becomes :class:`FaError`.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback.
+
+The functions carry the C names and mirror their argument order; outputs are
+caller-allocated tensors.  :func:`attention_fwd` / :func:`attention_bwd`
+allocate the outputs for convenience.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_status_string")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library():
+    """Load libfa.so; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m io_aware_tiled_fwd_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
+    lib.fa_fwd_f32.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
+    lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
+    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_bwd):
+        fn.restype = ctypes.c_int
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def _stream_handle(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _check4(t, name, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    return tuple(int(x) for x in q.shape)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _default_scale(d):
+    return 1.0 / math.sqrt(d)
+
+
+def fa_fwd(q, k, v, o, lse, causal=False, scale=None, stream=None) -> None:
+    """bf16 forward into caller-allocated o (bf16 [B,H,N,d]) and lse (fp32 [B,H,N])."""
+    B, H, N, d = _shape(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check4(t, n, torch.bfloat16)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{n} must have shape {(B, H, N, d)}")
+    _check4(lse, "lse", torch.float32)
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"lse must have shape {(B, H, N)}")
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, sc,
+                               int(bool(causal)), ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd")
+
+
+def fa_fwd_f32(q, k, v, o, lse, causal=False, scale=None, stream=None) -> None:
+    """fp32 forward into caller-allocated o (fp32 [B,H,N,d]) and lse (fp32 [B,H,N])."""
+    B, H, N, d = _shape(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check4(t, n, torch.float32)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{n} must have shape {(B, H, N, d)}")
+    _check4(lse, "lse", torch.float32)
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"lse must have shape {(B, H, N)}")
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, sc,
+                                   int(bool(causal)), ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_f32")
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, causal=False, scale=None, stream=None) -> None:
+    """bf16 backward into caller-allocated fp32 dq, dk, dv ([B,H,N,d]) and the
+    fp32 workspace delta ([B,H,N])."""
+    B, H, N, d = _shape(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check4(t, n, torch.bfloat16)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{n} must have shape {(B, H, N, d)}")
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check4(t, n, torch.float32)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{n} must have shape {(B, H, N, d)}")
+    for t, n in ((lse, "lse"), (delta, "delta")):
+        _check4(t, n, torch.float32)
+        if tuple(t.shape) != (B, H, N):
+            raise ValueError(f"{n} must have shape {(B, H, N)}")
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                               _ptr(dk), _ptr(dv), _ptr(delta), B, H, N, d, sc, int(bool(causal)),
+                               ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+
+
+def attention_fwd(q, k, v, causal=False, scale=None, stream=None):
+    """Allocating wrapper: returns (o, lse).  bf16 or fp32 inputs."""
+    B, H, N, d = _shape(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if q.dtype == torch.float32:
+        fa_fwd_f32(q, k, v, o, lse, causal, scale, stream)
+    else:
+        fa_fwd(q, k, v, o, lse, causal, scale, stream)
+    return o, lse
+
+
+def attention_bwd(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):
+    """Allocating wrapper: returns (dq, dk, dv) in fp32."""
+    B, H, N, d = _shape(q)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, causal, scale, stream)
+    return dq, dk, dv

@@ -60,16 +60,32 @@ def _load():
                                                       ctypes.c_int, ctypes.c_int]
         lib.oracle_attn_fwd_tiled.argtypes = [_f64p] * 5 + [_i64, _i64, _i64, ctypes.c_double,
                                                             ctypes.c_int, _i64, _i64, _i64, _f64p]
+        lib.oracle_attn_fwd_rows.argtypes = [_f64p] * 3 + [ctypes.POINTER(_i64), _i64, _f64p, _f64p,
+                                                           _i64, _i64, _i64, ctypes.c_double,
+                                                           ctypes.c_int, ctypes.c_int]
         lib.oracle_default_threads.argtypes = []
         for fn in (lib.oracle_attn_fwd, lib.oracle_attn_bwd, lib.oracle_attn_fwd_tiled,
-                   lib.oracle_default_threads):
+                   lib.oracle_attn_fwd_rows, lib.oracle_default_threads):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
 
 
 def default_threads() -> int:
-    return int(_load().oracle_default_threads())
+    """Threads the oracle uses by default: the CPUs this process may run on,
+    capped by OMP_NUM_THREADS when that is set (a GPU machine's CPU share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def _threads(threads):
+    return int(threads) if threads and threads > 0 else default_threads()
 
 
 def _as3(x, name):
@@ -99,7 +115,7 @@ def attn_fwd(q, k, v, scale, causal=False, threads=0):
     o = np.empty_like(q)
     lse = np.empty((BH, N), dtype=np.float64)
     _check(_load().oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), BH, N, d,
-                                   float(scale), int(bool(causal)), int(threads)), "oracle_attn_fwd")
+                                   float(scale), int(bool(causal)), _threads(threads)), "oracle_attn_fwd")
     return o, lse
 
 
@@ -114,7 +130,7 @@ def attn_bwd(q, k, v, dout, scale, causal=False, threads=0):
     delta = np.empty((BH, N), dtype=np.float64)
     _check(_load().oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
                                    _ptr(dv), _ptr(delta), BH, N, d, float(scale),
-                                   int(bool(causal)), int(threads)), "oracle_attn_bwd")
+                                   int(bool(causal)), _threads(threads)), "oracle_attn_bwd")
     return dq, dk, dv, delta
 
 
@@ -133,3 +149,22 @@ def attn_fwd_tiled(q, k, v, scale, causal=False, br=64, bc=64, trace_row=None):
         int(bool(causal)), int(br), int(bc), -1 if trace_row is None else int(trace_row),
         _ptr(trace) if trace is not None else None), "oracle_attn_fwd_tiled")
     return (o, lse) if trace is None else (o, lse, trace)
+
+
+def attn_fwd_rows(q, k, v, rows, scale, causal=False, threads=0):
+    """Forward for listed query rows only.  ``rows`` are flat indices
+    bh * N + i into the [BH, N] row space.  Returns (O [len(rows), d],
+    L [len(rows)])."""
+    q, k, v = _as3(q, "q"), _as3(k, "k"), _as3(v, "v")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must have one shape")
+    BH, N, d = q.shape
+    idx = np.ascontiguousarray(rows, dtype=np.int64)
+    o = np.empty((idx.size, d), dtype=np.float64)
+    lse = np.empty(idx.size, dtype=np.float64)
+    _check(_load().oracle_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v),
+                                        idx.ctypes.data_as(ctypes.POINTER(_i64)), idx.size,
+                                        _ptr(o), _ptr(lse), BH, N, d, float(scale),
+                                        int(bool(causal)), _threads(threads)),
+           "oracle_attn_fwd_rows")
+    return o, lse

@@ -116,42 +116,69 @@ typedef struct {
     int causal;
 } fwd_ctx;
 
+/* One query row r = bh * N + i: scores of the visible keys, their maximum,
+ * the softmax denominator, O_i = sum_j softmax_ij v_j and L_i = m + ln l. */
+static void fwd_one_row(const fwd_ctx* c, int64_t r, double* s, double* oi, double* lse_out) {
+    const int64_t N = c->N, d = c->d;
+    const int64_t bh = r / N, i = r % N;
+    const double* qi = c->q + r * d;
+    const double* kh = c->k + bh * N * d;
+    const double* vh = c->v + bh * N * d;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < N; ++j) {
+        if (!visible(c->causal, i, j)) continue;
+        double dot = 0.0;
+        for (int64_t t = 0; t < d; ++t) dot += qi[t] * kh[j * d + t];
+        s[j] = c->scale * dot;
+        if (s[j] > m) m = s[j];
+    }
+    for (int64_t t = 0; t < d; ++t) oi[t] = 0.0;
+    if (m == -INFINITY) { /* no visible key: O = 0, L = -inf */
+        *lse_out = -INFINITY;
+        return;
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < N; ++j)
+        if (visible(c->causal, i, j)) l += exp(s[j] - m);
+    for (int64_t j = 0; j < N; ++j) {
+        if (!visible(c->causal, i, j)) continue;
+        const double pij = exp(s[j] - m) / l;
+        for (int64_t t = 0; t < d; ++t) oi[t] += pij * vh[j * d + t];
+    }
+    *lse_out = m + log(l);
+}
+
 static void fwd_rows(void* p, int64_t begin, int64_t end) {
     fwd_ctx* c = (fwd_ctx*)p;
-    const int64_t N = c->N, d = c->d;
-    double* s = (double*)malloc(sizeof(double) * (size_t)N);
-    for (int64_t r = begin; r < end; ++r) { /* r = bh * N + i */
-        const int64_t bh = r / N, i = r % N;
-        const double* qi = c->q + r * d;
-        const double* kh = c->k + bh * N * d;
-        const double* vh = c->v + bh * N * d;
-        double* oi = c->o + r * d;
-        /* scores of the visible keys, and their maximum */
-        double m = -INFINITY;
-        for (int64_t j = 0; j < N; ++j) {
-            if (!visible(c->causal, i, j)) continue;
-            double dot = 0.0;
-            for (int64_t t = 0; t < d; ++t) dot += qi[t] * kh[j * d + t];
-            s[j] = c->scale * dot;
-            if (s[j] > m) m = s[j];
-        }
-        for (int64_t t = 0; t < d; ++t) oi[t] = 0.0;
-        if (m == -INFINITY) { /* no visible key: O = 0, L = -inf */
-            c->lse[r] = -INFINITY;
-            continue;
-        }
-        /* softmax denominator, then O = sum_j softmax_j * v_j */
-        double l = 0.0;
-        for (int64_t j = 0; j < N; ++j)
-            if (visible(c->causal, i, j)) l += exp(s[j] - m);
-        for (int64_t j = 0; j < N; ++j) {
-            if (!visible(c->causal, i, j)) continue;
-            const double pij = exp(s[j] - m) / l;
-            for (int64_t t = 0; t < d; ++t) oi[t] += pij * vh[j * d + t];
-        }
-        c->lse[r] = m + log(l);
-    }
+    double* s = (double*)malloc(sizeof(double) * (size_t)c->N);
+    for (int64_t r = begin; r < end; ++r) fwd_one_row(c, r, s, c->o + r * c->d, c->lse + r);
     free(s);
+}
+
+typedef struct {
+    fwd_ctx base;
+    const int64_t* rows;
+} fwd_rows_ctx;
+
+static void fwd_listed_rows(void* p, int64_t begin, int64_t end) {
+    fwd_rows_ctx* c = (fwd_rows_ctx*)p;
+    double* s = (double*)malloc(sizeof(double) * (size_t)c->base.N);
+    for (int64_t r = begin; r < end; ++r)
+        fwd_one_row(&c->base, c->rows[r], s, c->base.o + r * c->base.d, c->base.lse + r);
+    free(s);
+}
+
+/* Forward for listed query rows only (rows are independent): rows[r] is a flat
+ * index bh * N + i; o receives nrows x d values and lse nrows values. */
+int oracle_attn_fwd_rows(const double* q, const double* k, const double* v, const int64_t* rows,
+                         int64_t nrows, double* o, double* lse, int64_t BH, int64_t N, int64_t d,
+                         double scale, int causal, int nthreads) {
+    if (!q || !k || !v || !rows || !o || !lse || BH <= 0 || N <= 0 || d <= 0 || nrows < 0)
+        return ORACLE_ERR_ARG;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= BH * N) return ORACLE_ERR_ARG;
+    fwd_rows_ctx c = {{q, k, v, o, lse, N, d, scale, causal}, rows};
+    return parallel_for(nrows, nthreads, fwd_listed_rows, &c);
 }
 
 int oracle_attn_fwd(const double* q, const double* k, const double* v, double* o, double* lse,

@@ -1,0 +1,130 @@
+"""The C ABI without a GPU: the library loads, exports what include/fa.h
+declares, and rejects bad arguments before touching the device.
+
+Only calls that the library's argument checks reject are made here; those
+return before any HIP call, so no device is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    """Function names declared in include/*.h (int/const char* returning)."""
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from io_aware_tiled_fwd_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libfa.so is not built (python -m io_aware_tiled_fwd_amd.build)")
+    return binding.load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert set(declared_functions()) >= {"fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_status_string"}
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libfa.so does not export {name}"
+
+
+def test_binding_names_match_header():
+    from io_aware_tiled_fwd_amd import binding
+    assert set(binding.SYMBOLS) == set(declared_functions())
+    for name in binding.SYMBOLS:
+        assert callable(getattr(binding, name))
+
+
+def test_status_strings(lib):
+    from io_aware_tiled_fwd_amd import binding
+    assert binding.fa_status_string(0) == "FA_OK"
+    for st in (1, 2, 3):
+        assert binding.fa_status_string(st).startswith("FA_ERR_")
+    assert "unknown" in binding.fa_status_string(99)
+
+
+# A non-null, 16-byte aligned fake address: every call below is rejected by the
+# argument checks before any pointer is used or any kernel launched.
+FAKE = ctypes.c_void_p(0x1000)
+NUL = ctypes.c_void_p(0)
+
+
+def _fwd(lib, ptrs, B=1, H=1, N=16, d=64, scale=0.125, causal=0, f32=False):
+    fn = lib.fa_fwd_f32 if f32 else lib.fa_fwd
+    return fn(*ptrs, B, H, N, d, ctypes.c_float(scale), causal, NUL)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_fwd_rejects_bad_arguments(lib, f32):
+    ok = [FAKE] * 5
+    for i in range(5):  # each null pointer
+        ptrs = list(ok)
+        ptrs[i] = NUL
+        assert _fwd(lib, ptrs, f32=f32) == 1
+    assert _fwd(lib, ok, B=0, f32=f32) == 1
+    assert _fwd(lib, ok, H=-1, f32=f32) == 1
+    assert _fwd(lib, ok, N=0, f32=f32) == 1
+    assert _fwd(lib, ok, scale=float("nan"), f32=f32) == 1
+    assert _fwd(lib, ok, scale=float("inf"), f32=f32) == 1
+    assert _fwd(lib, ok, d=96, f32=f32) == 2
+    assert _fwd(lib, ok, d=256, f32=f32) == 2
+    assert _fwd(lib, ok, d=0, f32=f32) == 2
+    # 2^62 elements or more
+    assert _fwd(lib, ok, B=2 ** 20, H=2 ** 10, N=2 ** 25, d=128, f32=f32) == 1
+    # misaligned pointer
+    ptrs = list(ok)
+    ptrs[2] = ctypes.c_void_p(0x1002)
+    assert _fwd(lib, ptrs, f32=f32) == 1
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    ok = [FAKE] * 10
+
+    def call(ptrs, B=1, H=1, N=16, d=128, scale=0.1):
+        return lib.fa_bwd(*ptrs, B, H, N, d, ctypes.c_float(scale), 1, NUL)
+
+    for i in range(10):
+        ptrs = list(ok)
+        ptrs[i] = NUL
+        assert call(ptrs) == 1
+    assert call(ok, B=0) == 1
+    assert call(ok, scale=float("-inf")) == 1
+    assert call(ok, d=80) == 2
+    ptrs = list(ok)
+    ptrs[9] = ctypes.c_void_p(0x1004)
+    assert call(ptrs) == 1
+
+
+def test_package_import_does_not_load_library():
+    import importlib
+    import io_aware_tiled_fwd_amd.inputs  # noqa: F401
+    pkg = importlib.import_module("io_aware_tiled_fwd_amd")
+    assert "fa_fwd" in pkg.__all__
+
+
+def test_oracle_and_gpu_path_share_no_code():
+    """Neither side imports or includes the other."""
+    pkg = os.path.join(ROOT, "io_aware_tiled_fwd_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in re.sub(r"(#|//).*", "", text).lower() or f == "inputs.py", f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c", ".h")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "io_aware_tiled_fwd_amd" not in text and "fa_common" not in text, f
