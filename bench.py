@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark: exact tiled attention forward + backward on one MI355X.
+
+One step = the whole path on one batch: fa_fwd, then the backward's three
+stages (fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq), on synthetic bf16 inputs
+already resident in HBM.  Default workload: causal, B=2, H=32, N=8192, d=128
+(the shape the targets are stated at), Q/K/V/dO i.i.d. N(0,1).
+
+Counted FLOPs: forward 4 N^2 d B H, backward 10 N^2 d B H (2.5x forward), both
+halved under a causal mask.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 FLOP/clk)
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (B, H, N, d, causal)
+    "causal_fwdbwd_b2_h32_n8192_d128": (2, 32, 8192, 128, True),
+    "causal_fwdbwd_b4_h16_n4096_d128": (4, 16, 4096, 128, True),
+    "fwdbwd_b4_h16_n2048_d64": (4, 16, 2048, 64, False),
+    "fwdbwd_b1_h16_n18000_d128": (1, 16, 18000, 128, False),
+}
+DEFAULT_WORKLOAD = "causal_fwdbwd_b2_h32_n8192_d128"
+
+
+def counted_flops(B, H, N, d, causal):
+    f = 4.0 * N * N * d * B * H * (0.5 if causal else 1.0)
+    return f, 2.5 * f
+
+
+def kernel_flops(B, H, N, d, causal):
+    """Algorithmic MFMA FLOPs of each kernel per launch: every visible
+    (query, key) pair costs 2 d per matrix product the kernel performs
+    (fwd: S, PV; dK/dV: S, dP, dV, dK; dQ: S, dP, dQ)."""
+    pairs = N * N * B * H * (0.5 if causal else 1.0)
+    return {"fwd": 2 * 2 * d * pairs, "bwd_dkdv": 4 * 2 * d * pairs, "bwd_dq": 3 * 2 * d * pairs,
+            "bwd_preprocess": 2.0 * N * d * B * H}
+
+
+def kernel_bytes(B, H, N, d):
+    """Compulsory HBM bytes per launch (each tensor read or written once)."""
+    t = 2.0 * B * H * N * d  # one bf16 [B,H,N,d] tensor
+    f = 4.0 * B * H * N * d  # one fp32 [B,H,N,d] tensor
+    r = 4.0 * B * H * N      # one fp32 [B,H,N] vector
+    return {"fwd": 4 * t + r, "bwd_preprocess": 2 * t + r,
+            "bwd_dkdv": 4 * t + 2 * r + 2 * f, "bwd_dq": 4 * t + 2 * r + f}
+
+
+def cpu_baseline(heads, causal):
+    """The fp64 oracle, as it stands, on host cores: forward + backward of the
+    first few heads of the benchmark's own inputs (batch 0), each over all N
+    positions.  Rate = counted FLOPs of that sample / wall time."""
+    import oracle
+    from io_aware_tiled_fwd_amd import inputs
+
+    nh, n, d = heads["q"].shape
+    arr = [heads[x] for x in ("q", "k", "v", "do")]
+    scale = inputs.default_scale(d)
+    threads = oracle.default_threads()
+    oracle.attn_fwd(arr[0][:1, :8], arr[1][:1, :8], arr[2][:1, :8], scale, causal)  # load the library
+    t0 = time.perf_counter()
+    oracle.attn_fwd(*arr[:3], scale, causal, threads=threads)
+    oracle.attn_bwd(*arr, scale, causal, threads=threads)
+    dt = time.perf_counter() - t0
+    ff, fb = counted_flops(1, nh, n, d, causal)
+    return {"value": (ff + fb) / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"batch 0, heads 0..{nh - 1} of the same inputs (N={n}, d={d}), "
+                       f"{'causal ' if causal else ''}fwd+bwd in fp64; {dt:.2f} s wall, "
+                       f"counted FLOPs {ff + fb:.3e}"),
+            "seconds": dt}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8,
+                    help="heads of batch 0 the CPU baseline computes (about 10-20 s)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the forward and backward shard by (batch, head) with no communication).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from io_aware_tiled_fwd_amd import binding, inputs
+
+    binding.load_library()
+    B, H, N, d, causal = WORKLOADS[args.workload]
+    scale = inputs.default_scale(d)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ts = inputs.normal_qkv(B, H, N, d, seed=20263, with_dout=True)
+    t = {n: torch.from_numpy(ts.bits[n].view(np.int16)).view(torch.bfloat16).to(dev) for n in ts.names}
+    cpu_heads = {n: ts.f64[n][0, :max(1, min(args.cpu_heads, H))].copy() for n in ts.names}
+    del ts
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+    stream = torch.cuda.current_stream()
+    names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        binding.fa_fwd(t["q"], t["k"], t["v"], o, lse, causal, scale, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        binding.fa_bwd_preprocess(o, t["do"], delta, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        binding.fa_bwd_dkdv(t["q"], t["k"], t["v"], lse, t["do"], delta, dk, dv, causal, scale, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        binding.fa_bwd_dq(t["q"], t["k"], t["v"], lse, t["do"], delta, dq, causal, scale, stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {n: [] for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]))
+    med = {n: float(np.median(per[n])) for n in names}
+    avg = {n: float(np.mean(per[n])) for n in names}
+
+    ms_step = wall / args.steps * 1e3
+    ff, fb = counted_flops(B, H, N, d, causal)
+    value = (ff + fb) / (ms_step / 1e3) / 1e12
+    bwd_ms = med["bwd_preprocess"] + med["bwd_dkdv"] + med["bwd_dq"]
+    kflops = kernel_flops(B, H, N, d, causal)
+    kbytes = kernel_bytes(B, H, N, d)
+    kernels = {n: {"ms_median": round(med[n], 4), "ms_mean": round(avg[n], 4),
+                   "tflops": round(kflops[n] / (avg[n] / 1e3) / 1e12, 2),
+                   "gbs_compulsory": round(kbytes[n] / (avg[n] / 1e3) / 1e9, 1)} for n in names}
+    dominant = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: avg[n])
+    achieved = kflops[dominant] / (avg[dominant] / 1e3) / 1e12
+
+    out = {
+        "metric": "attention fwd/bwd TFLOP/s at B,H,N,d + % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: Q, K, V, dO i.i.d. N(0,1), bf16 (RNE), seed 20263",
+        "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                   "scale": scale, "flops_per_step_counted": ff + fb},
+        "fwd": {"tflops": round(ff / (med["fwd"] / 1e3) / 1e12, 2),
+                "frac_peak": round(ff / (med["fwd"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "ms": round(med["fwd"], 4)},
+        "bwd": {"tflops": round(fb / (bwd_ms / 1e3) / 1e12, 2),
+                "frac_peak": round(fb / (bwd_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "ms": round(bwd_ms, 4)},
+        "step_frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "kernels": kernels,
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "peak_bf16_tflops": PEAK_BF16_TFLOPS,
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(cpu_heads, causal)
+        out["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cb.items()
+                               if k != "seconds"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -21,7 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_status_string")
+SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
+           "fa_status_string")
 
 
 class FaError(RuntimeError):
@@ -47,7 +48,11 @@ def load_library():
     lib.fa_fwd.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_fwd_f32.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
-    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_bwd):
+    lib.fa_bwd_preprocess.argtypes = [vp] * 3 + [i, i, i, i, vp]
+    lib.fa_bwd_dkdv.argtypes = [vp] * 8 + [i, i, i, i, f, i, vp]
+    lib.fa_bwd_dq.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
+    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_bwd, lib.fa_bwd_preprocess, lib.fa_bwd_dkdv,
+               lib.fa_bwd_dq):
         fn.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -145,6 +150,61 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, causal=False, scale=None, s
                                ctypes.c_void_p(_stream_handle(stream)))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+
+
+def _check_bwd_args(q, k, v, dout, lse, delta, outs):
+    B, H, N, d = _shape(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _check4(t, n, torch.bfloat16)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{n} must have shape {(B, H, N, d)}")
+    for t, n in outs:
+        _check4(t, n, torch.float32)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{n} must have shape {(B, H, N, d)}")
+    for t, n in ((lse, "lse"), (delta, "delta")):
+        _check4(t, n, torch.float32)
+        if tuple(t.shape) != (B, H, N):
+            raise ValueError(f"{n} must have shape {(B, H, N)}")
+    return B, H, N, d
+
+
+def fa_bwd_preprocess(o, dout, delta, stream=None) -> None:
+    """delta = rowsum(dout * o) (fp32 [B,H,N]) from bf16 o and dout."""
+    B, H, N, d = _shape(o)
+    for t, n in ((o, "o"), (dout, "dout")):
+        _check4(t, n, torch.bfloat16)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{n} must have shape {(B, H, N, d)}")
+    _check4(delta, "delta", torch.float32)
+    if tuple(delta.shape) != (B, H, N):
+        raise ValueError(f"delta must have shape {(B, H, N)}")
+    st = load_library().fa_bwd_preprocess(_ptr(o), _ptr(dout), _ptr(delta), B, H, N, d,
+                                          ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_preprocess")
+
+
+def fa_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, causal=False, scale=None, stream=None) -> None:
+    """dK, dV (fp32) given lse and delta."""
+    B, H, N, d = _check_bwd_args(q, k, v, dout, lse, delta, ((dk, "dk"), (dv, "dv")))
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta),
+                                    _ptr(dk), _ptr(dv), B, H, N, d, sc, int(bool(causal)),
+                                    ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dkdv")
+
+
+def fa_bwd_dq(q, k, v, lse, dout, delta, dq, causal=False, scale=None, stream=None) -> None:
+    """dQ (fp32) given lse and delta."""
+    B, H, N, d = _check_bwd_args(q, k, v, dout, lse, delta, ((dq, "dq"),))
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta),
+                                  _ptr(dq), B, H, N, d, sc, int(bool(causal)),
+                                  ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dq")
 
 
 def attention_fwd(q, k, v, causal=False, scale=None, stream=None):

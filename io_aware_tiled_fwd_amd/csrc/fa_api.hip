@@ -65,6 +65,38 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
         fa::launch_bwd_bf16(q, k, v, o, lse, dO, dq, dk, dv, delta, B * H, N, d, scale, causal != 0, stream));
 }
 
+int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H, int N, int d,
+                      hipStream_t stream) {
+    if (!o || !dO || !delta) return FA_ERR_INVALID_ARG;
+    const int st = check_shape(B, H, N, d, 1.0f);
+    if (st != FA_OK) return st;
+    if (!aligned16(o) || !aligned16(dO) || !aligned16(delta)) return FA_ERR_INVALID_ARG;
+    return from_hip(fa::launch_bwd_preprocess(o, dO, delta, B * H, N, d, stream));
+}
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+                const float* delta, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
+                hipStream_t stream) {
+    if (!q || !k || !v || !lse || !dO || !delta || !dk || !dv) return FA_ERR_INVALID_ARG;
+    const int st = check_shape(B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    const void* ptrs[] = {q, k, v, lse, dO, delta, dk, dv};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+    return from_hip(fa::launch_bwd_dkdv(q, k, v, lse, dO, delta, dk, dv, B * H, N, d, scale, causal != 0, stream));
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO, const float* delta,
+              float* dq, int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
+    if (!q || !k || !v || !lse || !dO || !delta || !dq) return FA_ERR_INVALID_ARG;
+    const int st = check_shape(B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    const void* ptrs[] = {q, k, v, lse, dO, delta, dq};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+    return from_hip(fa::launch_bwd_dq(q, k, v, lse, dO, delta, dq, B * H, N, d, scale, causal != 0, stream));
+}
+
 const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "FA_OK";

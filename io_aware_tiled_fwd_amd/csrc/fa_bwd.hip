@@ -371,45 +371,80 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_bwd_t(const bf16* q, const bf16* k, const bf16* v, const bf16* o, const float* lse,
-                        const bf16* dout, float* dq, float* dk, float* dv, float* delta, int BH, int N,
-                        float scale, hipStream_t stream) {
+template <int D>
+hipError_t launch_pre_t(const bf16* o, const bf16* dout, float* delta, int BH, int N, hipStream_t stream) {
     const int64_t rows = (int64_t)BH * N;
     constexpr int rows_per_block = kBwdThreads / (D / 8);
-    const int pre_grid = (int)((rows + rows_per_block - 1) / rows_per_block);
-    hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3(pre_grid), dim3(kBwdThreads), 0, stream, o, dout,
-                       delta, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const float sl2 = scale * kLog2e;
+    const int grid = (int)((rows + rows_per_block - 1) / rows_per_block);
+    hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3(grid), dim3(kBwdThreads), 0, stream, o, dout, delta,
+                       rows);
+    return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv_t(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
+                         const float* delta, float* dk, float* dv, int BH, int N, float scale,
+                         hipStream_t stream) {
     const int nkb = (N + kDkvBkv - 1) / kDkvBkv;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(nkb * BH), dim3(kBwdThreads), 0, stream, q, k, v,
-                       dout, lse, delta, dk, dv, N, BH, nkb, sl2, scale);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+                       dout, lse, delta, dk, dv, N, BH, nkb, scale * kLog2e, scale);
+    return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dq_t(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
+                       const float* delta, float* dq, int BH, int N, float scale, hipStream_t stream) {
     const int nqb = (N + kDqBq - 1) / kDqBq;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(nqb * BH), dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                       lse, delta, dq, N, BH, nqb, sl2, scale);
+                       lse, delta, dq, N, BH, nqb, scale * kLog2e, scale);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                           const void* dout, float* dq, float* dk, float* dv, float* delta, int BH, int N,
-                           int d, float scale, bool causal, hipStream_t stream) {
+hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int BH, int N, int d,
+                                 hipStream_t stream) {
+    auto Op = static_cast<const bf16*>(o);
+    auto G = static_cast<const bf16*>(dout);
+    return d == 64 ? launch_pre_t<64>(Op, G, delta, BH, N, stream) : launch_pre_t<128>(Op, G, delta, BH, N, stream);
+}
+
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                           const float* delta, float* dk, float* dv, int BH, int N, int d, float scale,
+                           bool causal, hipStream_t stream) {
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
     auto V = static_cast<const bf16*>(v);
-    auto Op = static_cast<const bf16*>(o);
     auto G = static_cast<const bf16*>(dout);
-    if (d == 64) {
-        return causal ? launch_bwd_t<64, true>(Q, K, V, Op, lse, G, dq, dk, dv, delta, BH, N, scale, stream)
-                      : launch_bwd_t<64, false>(Q, K, V, Op, lse, G, dq, dk, dv, delta, BH, N, scale, stream);
-    }
-    return causal ? launch_bwd_t<128, true>(Q, K, V, Op, lse, G, dq, dk, dv, delta, BH, N, scale, stream)
-                  : launch_bwd_t<128, false>(Q, K, V, Op, lse, G, dq, dk, dv, delta, BH, N, scale, stream);
+    if (d == 64)
+        return causal ? launch_dkdv_t<64, true>(Q, K, V, lse, G, delta, dk, dv, BH, N, scale, stream)
+                      : launch_dkdv_t<64, false>(Q, K, V, lse, G, delta, dk, dv, BH, N, scale, stream);
+    return causal ? launch_dkdv_t<128, true>(Q, K, V, lse, G, delta, dk, dv, BH, N, scale, stream)
+                  : launch_dkdv_t<128, false>(Q, K, V, lse, G, delta, dk, dv, BH, N, scale, stream);
+}
+
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                         const float* delta, float* dq, int BH, int N, int d, float scale, bool causal,
+                         hipStream_t stream) {
+    auto Q = static_cast<const bf16*>(q);
+    auto K = static_cast<const bf16*>(k);
+    auto V = static_cast<const bf16*>(v);
+    auto G = static_cast<const bf16*>(dout);
+    if (d == 64)
+        return causal ? launch_dq_t<64, true>(Q, K, V, lse, G, delta, dq, BH, N, scale, stream)
+                      : launch_dq_t<64, false>(Q, K, V, lse, G, delta, dq, BH, N, scale, stream);
+    return causal ? launch_dq_t<128, true>(Q, K, V, lse, G, delta, dq, BH, N, scale, stream)
+                  : launch_dq_t<128, false>(Q, K, V, lse, G, delta, dq, BH, N, scale, stream);
+}
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, float* dq, float* dk, float* dv, float* delta, int BH, int N,
+                           int d, float scale, bool causal, hipStream_t stream) {
+    hipError_t e = launch_bwd_preprocess(o, dout, delta, BH, N, d, stream);
+    if (e != hipSuccess) return e;
+    e = launch_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, BH, N, d, scale, causal, stream);
+    if (e != hipSuccess) return e;
+    return launch_bwd_dq(q, k, v, lse, dout, delta, dq, BH, N, d, scale, causal, stream);
 }
 
 }  // namespace fa

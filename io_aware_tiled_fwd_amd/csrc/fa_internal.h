@@ -15,4 +15,14 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            const void* dout, float* dq, float* dk, float* dv, float* delta, int BH, int N,
                            int d, float scale, bool causal, hipStream_t stream);
 
+// The backward's stages, individually.
+hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int BH, int N, int d,
+                                 hipStream_t stream);
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                           const float* delta, float* dk, float* dv, int BH, int N, int d, float scale,
+                           bool causal, hipStream_t stream);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                         const float* delta, float* dq, int BH, int N, int d, float scale, bool causal,
+                         hipStream_t stream);
+
 }  // namespace fa
