@@ -35,8 +35,11 @@
  *  - Arguments are validated before any launch; on an error nothing is
  *    launched and outputs are untouched.  No exception crosses the ABI.
  *
- * Supported shapes: B, H, N >= 1 with B*H <= 2^31-1 and B*H*N*d < 2^62
- * (element offsets are 64-bit), d in {64, 128}.
+ * Supported shapes: B, H, N >= 1 with B*H <= 2^31-1, B*H*N*d < 2^62 (element
+ * offsets are 64-bit), N*d*4 < 2^31 (one head is addressed through a 32-bit
+ * buffer range: N <= 4194303 at d = 128), d in {64, 128}.
+ * Inputs must be finite: the kernels are built without IEEE NaN handling, so
+ * NaN or infinite inputs give unspecified outputs.
  */
 #ifndef FA_H
 #define FA_H

@@ -3,7 +3,8 @@
     python -m io_aware_tiled_fwd_amd.build          # compile csrc/*.hip -> libfa.so
 
 Every object is rebuilt on each call (the build is the "does it compile"
-check).  Packed-fp32 VALU instructions are disabled for all device code.
+check).  Packed-fp32 VALU instructions are disabled for all device code, and
+device code runs with IEEE NaN handling off (inputs must be finite).
 """
 from __future__ import annotations
 
@@ -35,6 +36,9 @@ def flags() -> list:
     return [
         "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # Scores are finite or -inf by construction: without IEEE NaN quieting,
+        # max/min need no canonicalising instructions.
+        "-Xarch_device", "-mno-amdgpu-ieee", "-Xarch_device", "-fno-honor-nans",
         "-Wall", "-Wno-unused-function",
         "-I", INCLUDE, "-I", CSRC,
     ]

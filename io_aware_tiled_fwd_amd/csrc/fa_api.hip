@@ -23,6 +23,8 @@ int check_shape(int B, int H, int N, int d, float scale) {
     // Element offsets are 64-bit; also keep the flat workgroup count < 2^31.
     if ((double)bh * (double)N * (double)d >= 4.611686018427388e18) return FA_ERR_INVALID_ARG;  // 2^62
     if ((double)bh * (double)((N + 63) / 64) >= 2147483647.0) return FA_ERR_INVALID_ARG;
+    // One head of one fp32 [N, d] tensor is addressed through a 32-bit byte range.
+    if ((double)N * (double)d * 4.0 > 2147483647.0) return FA_ERR_INVALID_ARG;
     return FA_OK;
 }
 

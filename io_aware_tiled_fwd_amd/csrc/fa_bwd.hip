@@ -15,6 +15,9 @@
 //                   registers and are written once.
 //   3. dQ           one workgroup per 128 query rows (32 per wavefront),
 //                   walking the key tiles; dQ accumulates in registers.
+// Tiles are staged row-major in double-buffered LDS through buffer loads (rows
+// past N read as zero); operands that must be transposed (dO^T, Q^T, K^T) are
+// read with the gfx950 transposing LDS read, so no transposed copy is stored.
 // dQ is produced without atomics, so the backward is bitwise reproducible (the
 // deep-dive page's pitfalls section warns that atomic dQ accumulation is not).
 //
@@ -30,53 +33,37 @@ namespace {
 
 constexpr int kBwdThreads = 256;
 
-// Stages a [ROWS x D] bf16 tile from HBM through registers into LDS, row-major
-// and/or transposed.  Each thread loads G consecutive rows x 8 dims (G 16-byte
-// loads); the transposed copy puts those G values of each dim next to each
-// other at key_slot(row), i.e. one 8- or 4-byte LDS store per dim.
+// Row stride (elements) of a bf16 [rows][D] LDS tile that is read both as
+// 16-byte rows (MFMA operand M) and through ds_read_b64_tr_b16 (operand M^T):
+// 16 consecutive rows of one 16-byte column, and 4 consecutive rows of 32
+// bytes, each fall on distinct banks (measured on gfx950).
+template <int D>
+constexpr int both_ways_stride() { return D == 128 ? D + 24 : D + 8; }
+
+// Stages a [ROWS x D] bf16 tile: HBM -> registers (buffer loads, rows past the
+// end read as zero) -> row-major LDS.  Thread t holds rows (t + 256 r) / DCH,
+// 16-byte column t % DCH, r < CH.  The tile offset is a scalar, so the per-lane
+// VGPR offset is fixed for the kernel's lifetime.
 template <int D, int ROWS>
 struct TileStager {
     static constexpr int DCH = D / 8;
-    static constexpr int G = ROWS * DCH / kBwdThreads;  // rows per thread
-    static constexpr int DCH_PER_WAVE = DCH / 4;
-    static_assert(G == 2 || G == 4, "rows per thread");
-    static_assert(G * kBwdThreads == ROWS * DCH, "tile split");
-
-    u32x4 reg[G];
-    int dch, grp;
-
-    __device__ explicit TileStager(int tid) {
-        const int w = tid >> 6, lane = tid & 63;
-        dch = w * DCH_PER_WAVE + lane % DCH_PER_WAVE;
-        grp = lane / DCH_PER_WAVE;
+    static constexpr int CH = ROWS * DCH / kBwdThreads;
+    static constexpr int ROWS_PER_PASS = kBwdThreads / DCH;
+    static_assert(CH * kBwdThreads == ROWS * DCH, "tile split");
+    u32x4 reg[CH];
+    int voff, lds_off;
+    __device__ TileStager(int tid, int stride) {
+        voff = ((tid / DCH) * D + 8 * (tid % DCH)) * 2;
+        lds_off = (tid / DCH) * stride + 8 * (tid % DCH);
     }
-    // src points at row 0 of the head; rows >= N read as zero.
-    __device__ void load(const bf16* src, int row0, int N) {
+    __device__ void load(__amdgpu_buffer_rsrc_t rs, int row0) {
 #pragma unroll
-        for (int kk = 0; kk < G; ++kk) {
-            const int row = row0 + grp * G + kk;
-            reg[kk] = row < N ? *reinterpret_cast<const u32x4*>(src + (int64_t)row * D + 8 * dch) : u32x4{};
-        }
+        for (int r = 0; r < CH; ++r) reg[r] = buffer_load16(rs, voff + r * ROWS_PER_PASS * D * 2, row0 * D * 2);
     }
-    __device__ void store_rows(bf16* lds, int stride) const {
+    __device__ void store(bf16* lds, int stride) const {
 #pragma unroll
-        for (int kk = 0; kk < G; ++kk)
-            *reinterpret_cast<u32x4*>(&lds[(grp * G + kk) * stride + 8 * dch]) = reg[kk];
-    }
-    __device__ void store_transposed(bf16* lds, int stride) const {
-        const int slot0 = key_slot(grp * G);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            uint32_t e[G];
-#pragma unroll
-            for (int kk = 0; kk < G; ++kk) e[kk] = (reg[kk][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
-            bf16* dst = &lds[(8 * dch + t) * stride + slot0];
-            if constexpr (G == 4) {
-                *reinterpret_cast<u32x2*>(dst) = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-            } else {
-                *reinterpret_cast<uint32_t*>(dst) = e[0] | (e[1] << 16);
-            }
-        }
+        for (int r = 0; r < CH; ++r)
+            *reinterpret_cast<u32x4*>(&lds[lds_off + r * ROWS_PER_PASS * stride]) = reg[r];
     }
 };
 
@@ -106,16 +93,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_preprocess_kernel(const bf16*
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK, dV.  Per query block of 64 rows, staged in LDS:
-//      Q   row-major [64][d]  and  Q^T  [d][64 slots]
-//      dO  row-major [64][d]  and  dO^T [d][64 slots]
-//      L (log2 domain, +inf past N) and D.
+// 2. dK, dV.  Per block of 64 query rows, staged row-major in LDS (double
+//    buffered): Q, dO, L (log2 domain, +inf past N) and D.
 //    Per wavefront (32 keys) and 32-query half, with C tiles [query x key]:
 //      S  = Q K^T            (A = Q rows from LDS, B = K^T from registers)
 //      dP = dO V^T           (A = dO rows from LDS, B = V^T from registers)
 //      P  = exp2(S c - L2), dS = P (dP - D)
-//      dV^T += dO^T P        (A = dO^T from LDS, B = P from registers)
-//      dK^T += Q^T dS        (A = Q^T from LDS, B = dS from registers)
+//      dV^T += dO^T P        (A = dO^T: transposing LDS reads; B = P from registers)
+//      dK^T += Q^T dS        (A = Q^T:  transposing LDS reads; B = dS from registers)
 
 constexpr int kDkvBq = 64;    // query rows per step
 constexpr int kDkvBkv = 128;  // keys per workgroup
@@ -126,36 +111,38 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     float* __restrict__ dK, float* __restrict__ dV, int N, int BH, int nkb, float scale_log2, float scale) {
     constexpr int BQ = kDkvBq;
-    constexpr int RS = D + 8;   // row-major stride
-    constexpr int TS = BQ + 8;  // transposed stride
-    __shared__ __attribute__((aligned(16))) bf16 sQ[BQ * RS];
-    __shared__ __attribute__((aligned(16))) bf16 sQt[D * TS];
-    __shared__ __attribute__((aligned(16))) bf16 sdO[BQ * RS];
-    __shared__ __attribute__((aligned(16))) bf16 sdOt[D * TS];
-    __shared__ __attribute__((aligned(16))) float sL[BQ];
-    __shared__ __attribute__((aligned(16))) float sD[BQ];
+    constexpr int RS = both_ways_stride<D>();
+    __shared__ __attribute__((aligned(16))) bf16 sQ[2][BQ * RS];
+    __shared__ __attribute__((aligned(16))) bf16 sdO[2][BQ * RS];
+    __shared__ __attribute__((aligned(16))) float sL[2][BQ];
+    __shared__ __attribute__((aligned(16))) float sD[2][BQ];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int lq = lane & 31, h = lane >> 5;
-    // Flat id -> (head, key block); key blocks ascend, so for causal masks the
-    // heaviest blocks (the first ones, seen by the most queries) start first.
-    const int bh = blockIdx.x % BH;
-    const int kb = blockIdx.x / BH;
+    // Flat id -> (head, key block): XCD-contiguous, head-major; key blocks
+    // ascend, so for causal masks the heaviest blocks (the first ones, seen by
+    // the most queries) start first.
+    const int task = xcd_task(blockIdx.x, BH * nkb);
+    if (task >= BH * nkb) return;
+    const int bh = task / nkb;
+    const int kb = task % nkb;
     const int k0 = kb * kDkvBkv;
     const int kw0 = k0 + 32 * w;
     const int key = kw0 + lq;
     const int64_t base = (int64_t)bh * N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + base, head_bytes);
 
-    // K^T and V^T operands of this lane's key.
+    // K^T and V^T operands of this lane's key (zero past N).
     bf16x8 kf[D / 16], vf[D / 16];
+    {
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        if (key < N) {
-            kf[ks] = *reinterpret_cast<const bf16x8*>(K + base + (int64_t)key * D + 16 * ks + 8 * h);
-            vf[ks] = *reinterpret_cast<const bf16x8*>(V + base + (int64_t)key * D + 16 * ks + 8 * h);
-        } else {
-            kf[ks] = bf16x8{};
-            vf[ks] = bf16x8{};
+        for (int ks = 0; ks < D / 16; ++ks) {
+            kf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(krs, (lq * D + 16 * ks + 8 * h) * 2, kw0 * D * 2));
+            vf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(vrs, (lq * D + 16 * ks + 8 * h) * 2, kw0 * D * 2));
         }
     }
     f32x16 dkacc[D / 32], dvacc[D / 32];
@@ -167,76 +154,87 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 
     const int nqblk = (N + BQ - 1) / BQ;
     const int iq0 = CAUSAL ? k0 / BQ : 0;
-    TileStager<D, BQ> stq(tid), stdo(tid);
+    TileStager<D, BQ> stq(tid, RS), stg(tid, RS);
     float lreg = 0.f, dreg = 0.f;
+    const float* lse_h = LSE + (int64_t)bh * N;
+    const float* d_h = Dl + (int64_t)bh * N;
     auto load_block = [&](int iq) {
         const int i0 = iq * BQ;
-        stq.load(Q + base, i0, N);
-        stdo.load(dO + base, i0, N);
+        stq.load(qrs, i0);
+        stg.load(grs, i0);
         if (tid < BQ) {
-            const int r = i0 + tid;
-            lreg = r < N ? LSE[(int64_t)bh * N + r] * kLog2e : INFINITY;
-            dreg = r < N ? Dl[(int64_t)bh * N + r] : 0.f;
+            const int r = min(i0 + tid, N - 1);
+            lreg = i0 + tid < N ? lse_h[r] * kLog2e : INFINITY;  // P = 0 past N
+            dreg = i0 + tid < N ? d_h[r] : 0.f;
         }
     };
-    if (iq0 < nqblk) load_block(iq0);
-    for (int iq = iq0; iq < nqblk; ++iq) {
-        __syncthreads();
-        stq.store_rows(sQ, RS);
-        stq.store_transposed(sQt, TS);
-        stdo.store_rows(sdO, RS);
-        stdo.store_transposed(sdOt, TS);
+    auto store_block = [&](int buf) {
+        stq.store(sQ[buf], RS);
+        stg.store(sdO[buf], RS);
         if (tid < BQ) {
-            sL[tid] = lreg;
-            sD[tid] = dreg;
+            sL[buf][tid] = lreg;
+            sD[buf][tid] = dreg;
         }
-        __syncthreads();
-        if (iq + 1 < nqblk) load_block(iq + 1);
+    };
+    // Per-lane LDS offsets: 16-byte rows and transposing reads.
+    const int row_off = lq * RS + 8 * h;
+    const int tr_off = tr_row(lane) * RS + tr_col(lane);
 
+    // Loads and stores are unconditional (the last step re-stages the final
+    // block into the idle buffer) so that no math waits on a pending load.
+    if (iq0 < nqblk) {
+        load_block(iq0);
+        store_block(0);
+    }
+    __syncthreads();
+    for (int iq = iq0; iq < nqblk; ++iq) {
+        const int buf = (iq - iq0) & 1;
+        load_block(min(iq + 1, nqblk - 1));
         const int i0 = iq * BQ;
-        if (CAUSAL && i0 + BQ - 1 < kw0) continue;  // every query precedes every key of this wave
-        const bool diag = CAUSAL && (i0 < kw0 + 31);
-
+        // Skip blocks whose every query precedes every key of this wave.
+        if (!CAUSAL || __builtin_amdgcn_readfirstlane(i0 + BQ - 1 >= kw0)) {
+            const bool diag = CAUSAL && __builtin_amdgcn_readfirstlane(i0 < kw0 + 31);
+            const bf16* qt = sQ[buf];
+            const bf16* gt = sdO[buf];
 #pragma unroll
-        for (int qh = 0; qh < BQ / 32; ++qh) {
-            f32x16 s = f32x16{}, dp = f32x16{};
-            const bf16* qp = &sQ[(32 * qh + lq) * RS + 8 * h];
-            const bf16* gp = &sdO[(32 * qh + lq) * RS + 8 * h];
+            for (int qh = 0; qh < BQ / 32; ++qh) {
+                f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                s = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(qp + 16 * ks), kf[ks], s);
-                dp = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(gp + 16 * ks), vf[ks], dp);
-            }
-            // Register i holds query 32 qh + c_row(i, h); four consecutive queries per float4.
-            bf16x8 pf[2], dsf[2];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[32 * qh + 8 * r + 4 * h]);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[32 * qh + 8 * r + 4 * h]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * r + e;
-                    float p = fast_exp2(fmaf(s[i], scale_log2, -l4[e]));
-                    if (diag && key > i0 + 32 * qh + c_row(i, h)) p = 0.f;
-                    const float ds = p * (dp[i] - d4[e]);
-                    pf[i >> 3][i & 7] = (bf16)p;
-                    dsf[i >> 3][i & 7] = (bf16)ds;
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    s = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(qt + 32 * qh * RS + row_off + 16 * ks),
+                                           kf[ks], s);
+                    dp = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(gt + 32 * qh * RS + row_off + 16 * ks),
+                                            vf[ks], dp);
                 }
-            }
-            // k-step s2 of this half covers queries 32 qh + 16 s2 .. +15 (slots 16 s2 + 8 h + j).
+                // Register i holds query 32 qh + c_row(i, h); four consecutive queries per float4.
+                bf16x8 pf[2], dsf[2];
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const bf16* gtp = &sdOt[(32 * db + lq) * TS + 32 * qh + 8 * h];
-                const bf16* qtp = &sQt[(32 * db + lq) * TS + 32 * qh + 8 * h];
+                for (int r = 0; r < 4; ++r) {
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][32 * qh + 8 * r + 4 * h]);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[buf][32 * qh + 8 * r + 4 * h]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * r + e;
+                        float p = fast_exp2(fmaf(s[i], scale_log2, -l4[e]));
+                        if (diag && key > i0 + 32 * qh + c_row(i, h)) p = 0.f;
+                        pf[i >> 3][i & 7] = (bf16)p;
+                        dsf[i >> 3][i & 7] = (bf16)(p * (dp[i] - d4[e]));
+                    }
+                }
+                // k-step s2 covers queries 32 qh + 16 s2 + {4h + e, 8 + 4h + e}.
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    dvacc[db] = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(gtp + 16 * s2), pf[s2],
-                                                   dvacc[db]);
-                    dkacc[db] = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(qtp + 16 * s2), dsf[s2],
-                                                   dkacc[db]);
+                    const int off = (32 * qh + 16 * s2) * RS + tr_off;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        dvacc[db] = mfma_bf16_32x32x16(lds_read_tr_a(gt + off + 32 * db, RS), pf[s2], dvacc[db]);
+                        dkacc[db] = mfma_bf16_32x32x16(lds_read_tr_a(qt + off + 32 * db, RS), dsf[s2], dkacc[db]);
+                    }
                 }
             }
         }
+        store_block(buf ^ 1);
+        __syncthreads();
     }
 
     // Register i of block db holds dim 32 db + c_row(i, h) of this lane's key.
@@ -257,13 +255,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ.  Per key tile of 64 keys, staged in LDS:
-//      K row-major [64][d],  K^T [d][64 slots],  V row-major [64][d].
+// 3. dQ.  Per tile of 64 keys, staged row-major in LDS (double buffered): K
+//    (read both as rows and transposed) and V (rows).
 //    Per wavefront (32 queries) and 32-key half, with C tiles [key x query]:
 //      S^T  = K Q^T      (A = K rows from LDS, B = Q^T from registers)
 //      dP^T = V dO^T     (A = V rows from LDS, B = dO^T from registers)
 //      P^T = exp2(S^T c - L2), dS^T = P^T (dP^T - D)
-//      dQ^T += K^T dS^T  (A = K^T from LDS, B = dS^T from registers)
+//      dQ^T += K^T dS^T  (A = K^T: transposing LDS reads; B = dS^T from registers)
 
 constexpr int kDqBq = 128;  // query rows per workgroup
 constexpr int kDqBkv = 64;  // keys per step
@@ -274,35 +272,39 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     float* __restrict__ dQ, int N, int BH, int nqb, float scale_log2, float scale) {
     constexpr int BKV = kDqBkv;
-    constexpr int RS = D + 8;
-    constexpr int TS = BKV + 8;
-    __shared__ __attribute__((aligned(16))) bf16 sK[BKV * RS];
-    __shared__ __attribute__((aligned(16))) bf16 sKt[D * TS];
-    __shared__ __attribute__((aligned(16))) bf16 sV[BKV * RS];
+    constexpr int KS = both_ways_stride<D>();
+    constexpr int VS = D + 8;  // rows only
+    __shared__ __attribute__((aligned(16))) bf16 sK[2][BKV * KS];
+    __shared__ __attribute__((aligned(16))) bf16 sV[2][BKV * VS];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int lq = lane & 31, h = lane >> 5;
-    const int bh = blockIdx.x % BH;
-    const int qi = blockIdx.x / BH;
+    const int task = xcd_task(blockIdx.x, BH * nqb);
+    if (task >= BH * nqb) return;
+    const int bh = task / nqb;
+    const int qi = task % nqb;
     const int qb = CAUSAL ? (nqb - 1 - qi) : qi;  // heaviest query blocks first
     const int q0 = qb * kDqBq;
     const int qw0 = q0 + 32 * w;
     const int qrow = qw0 + lq;
     const int64_t base = (int64_t)bh * N * D;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
 
     bf16x8 qf[D / 16], gf[D / 16];
+    {
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
+        const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + base, head_bytes);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        if (qrow < N) {
-            qf[ks] = *reinterpret_cast<const bf16x8*>(Q + base + (int64_t)qrow * D + 16 * ks + 8 * h);
-            gf[ks] = *reinterpret_cast<const bf16x8*>(dO + base + (int64_t)qrow * D + 16 * ks + 8 * h);
-        } else {
-            qf[ks] = bf16x8{};
-            gf[ks] = bf16x8{};
+        for (int ks = 0; ks < D / 16; ++ks) {
+            qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(qrs, (lq * D + 16 * ks + 8 * h) * 2, qw0 * D * 2));
+            gf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(grs, (lq * D + 16 * ks + 8 * h) * 2, qw0 * D * 2));
         }
     }
-    const float l2 = qrow < N ? LSE[(int64_t)bh * N + qrow] * kLog2e : 0.f;
-    const float dq_d = qrow < N ? Dl[(int64_t)bh * N + qrow] : 0.f;
+    const int qr = min(qrow, N - 1);
+    const float l2 = qrow < N ? LSE[(int64_t)bh * N + qr] * kLog2e : 0.f;
+    const float dq_d = qrow < N ? Dl[(int64_t)bh * N + qr] : 0.f;
 
     f32x16 dqacc[D / 32];
 #pragma unroll
@@ -310,53 +312,58 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
 
     int ntiles = (N + BKV - 1) / BKV;
     if (CAUSAL) ntiles = min(ntiles, (min(q0 + kDqBq, N) - 1) / BKV + 1);
-    TileStager<D, BKV> stk(tid), stv(tid);
-    if (ntiles > 0) {
-        stk.load(K + base, 0, N);
-        stv.load(V + base, 0, N);
-    }
-    for (int j = 0; j < ntiles; ++j) {
-        __syncthreads();
-        stk.store_rows(sK, RS);
-        stk.store_transposed(sKt, TS);
-        stv.store_rows(sV, RS);
-        __syncthreads();
-        if (j + 1 < ntiles) {
-            stk.load(K + base, (j + 1) * BKV, N);
-            stv.load(V + base, (j + 1) * BKV, N);
-        }
-        const int k0 = j * BKV;
-        if (CAUSAL && k0 > qw0 + 31) continue;
-        const bool mask = (k0 + BKV > N) || (CAUSAL && k0 + BKV - 1 > qw0);
+    TileStager<D, BKV> stk(tid, KS), stv(tid, VS);
+    const int k_off = lq * KS + 8 * h;
+    const int v_off = lq * VS + 8 * h;
+    const int tr_off = tr_row(lane) * KS + tr_col(lane);
 
-        bf16x8 dsf[BKV / 16];
+    stk.load(krs, 0);
+    stv.load(vrs, 0);
+    stk.store(sK[0], KS);
+    stv.store(sV[0], VS);
+    __syncthreads();
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        const int jn = min(j + 1, ntiles - 1);
+        stk.load(krs, jn * BKV);
+        stv.load(vrs, jn * BKV);
+        const int k0 = j * BKV;
+        if (!CAUSAL || __builtin_amdgcn_readfirstlane(k0 <= qw0 + 31)) {
+            const bool mask = __builtin_amdgcn_readfirstlane((k0 + BKV > N) || (CAUSAL && k0 + BKV - 1 > qw0));
+            const bf16* kt = sK[buf];
+            const bf16* vt = sV[buf];
+            bf16x8 dsf[BKV / 16];
 #pragma unroll
-        for (int kh = 0; kh < BKV / 32; ++kh) {
-            f32x16 s = f32x16{}, dp = f32x16{};
-            const bf16* kp = &sK[(32 * kh + lq) * RS + 8 * h];
-            const bf16* vp = &sV[(32 * kh + lq) * RS + 8 * h];
+            for (int kh = 0; kh < BKV / 32; ++kh) {
+                f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                s = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(kp + 16 * ks), qf[ks], s);
-                dp = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(vp + 16 * ks), gf[ks], dp);
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float p = fast_exp2(fmaf(s[i], scale_log2, -l2));
-                if (mask) {
-                    const int kk = k0 + 32 * kh + c_row(i, h);
-                    if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    s = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(kt + 32 * kh * KS + k_off + 16 * ks),
+                                           qf[ks], s);
+                    dp = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(vt + 32 * kh * VS + v_off + 16 * ks),
+                                            gf[ks], dp);
                 }
-                dsf[2 * kh + (i >> 3)][i & 7] = (bf16)(p * (dp[i] - dq_d));
-            }
-        }
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const bf16* ktp = &sKt[(32 * db + lq) * TS + 8 * h];
+                for (int i = 0; i < 16; ++i) {
+                    float p = fast_exp2(fmaf(s[i], scale_log2, -l2));
+                    if (mask) {
+                        const int kk = k0 + 32 * kh + c_row(i, h);
+                        if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
+                    }
+                    dsf[2 * kh + (i >> 3)][i & 7] = (bf16)(p * (dp[i] - dq_d));
+                }
+            }
+            // dQ^T += K^T dS^T; k-step s2 covers keys 16 s2 + {4h + e, 8 + 4h + e}.
 #pragma unroll
             for (int s2 = 0; s2 < BKV / 16; ++s2)
-                dqacc[db] = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(ktp + 16 * s2), dsf[s2], dqacc[db]);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    dqacc[db] = mfma_bf16_32x32x16(lds_read_tr_a(kt + 16 * s2 * KS + tr_off + 32 * db, KS), dsf[s2],
+                                                   dqacc[db]);
         }
+        stk.store(sK[buf ^ 1], KS);
+        stv.store(sV[buf ^ 1], VS);
+        __syncthreads();
     }
 
     if (qrow < N) {
@@ -386,7 +393,7 @@ hipError_t launch_dkdv_t(const bf16* q, const bf16* k, const bf16* v, const floa
                          const float* delta, float* dk, float* dv, int BH, int N, float scale,
                          hipStream_t stream) {
     const int nkb = (N + kDkvBkv - 1) / kDkvBkv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(nkb * BH), dim3(kBwdThreads), 0, stream, q, k, v,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(grid_for_tasks(nkb * BH)), dim3(kBwdThreads), 0, stream, q, k, v,
                        dout, lse, delta, dk, dv, N, BH, nkb, scale * kLog2e, scale);
     return hipGetLastError();
 }
@@ -395,7 +402,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
                        const float* delta, float* dq, int BH, int N, float scale, hipStream_t stream) {
     const int nqb = (N + kDqBq - 1) / kDqBq;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(nqb * BH), dim3(kBwdThreads), 0, stream, q, k, v, dout,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(grid_for_tasks(nqb * BH)), dim3(kBwdThreads), 0, stream, q, k, v, dout,
                        lse, delta, dq, N, BH, nqb, scale * kLog2e, scale);
     return hipGetLastError();
 }

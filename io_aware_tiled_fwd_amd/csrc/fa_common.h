@@ -54,6 +54,74 @@ __device__ __forceinline__ f32x16 mfma_f32_32x32x2(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane 16g + r receives element r%4 of the 8-byte chunks addressed by
+// lanes 16g + 4e + r/4, e = 0..3 (checked on hardware).  Two such reads give
+// the 8-element A operand of v_mfma_f32_32x32x16_bf16 for A = M^T, M stored
+// row-major in LDS: see tr_row / tr_col.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+// For A[m][k] = M[k][m] over a 32(m) x 16(k) block: lane l points its first
+// read at M[tr_row(l)][tr_col(l)] and its second at M[tr_row(l) + 8][tr_col(l)].
+// Lane half h = l/32 then holds k = 4h + e (first read) and 8 + 4h + e (second
+// read): the k-order of a C tile's rows c_row(), so a score tile's registers
+// can be the matching B operand without any shuffle.
+__device__ __forceinline__ constexpr int tr_row(int lane) { return 4 * (lane >> 5) + ((lane & 15) >> 2); }
+__device__ __forceinline__ constexpr int tr_col(int lane) { return 16 * ((lane >> 4) & 1) + 4 * (lane & 3); }
+__device__ __forceinline__ bf16x8 lds_read_tr_a(const bf16* p, int row_stride) {
+    const bf16x4 lo = lds_read_tr(p), hi = lds_read_tr(p + 8 * row_stride);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2).
+// xcd_task() turns the flat id into a task index such that every XCD receives
+// a contiguous range of tasks; launch grid_for_tasks(total) workgroups and let
+// those with task >= total exit.  With tasks ordered head-major, the query
+// blocks of one head run together on one XCD and share its K/V in that L2.
+constexpr int kNumXcd = 8;
+__host__ __device__ __forceinline__ constexpr int grid_for_tasks(int total) {
+    return kNumXcd * ((total + kNumXcd - 1) / kNumXcd);
+}
+__device__ __forceinline__ int xcd_task(int id, int total) {
+    const int per = (total + kNumXcd - 1) / kNumXcd;
+    return (id % kNumXcd) * per + id / kNumXcd;
+}
+
+// Buffer resource over [base, base + bytes): raw buffer loads whose byte offset
+// (VGPR offset + SGPR offset) falls outside return zero (range checking of
+// untyped buffer loads; the SGPR offset takes part, checked on hardware).  A
+// ragged last tile therefore needs no branches: rows past N read as 0.
+// The base and size are made wave-uniform explicitly so that the descriptor
+// lives in SGPRs (a descriptor in VGPRs forces a loop around every load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+// Index of the calling wavefront in its workgroup, as a scalar (wave-uniform)
+// value so that branches on it are scalar branches.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Maximum of the 32 score registers of two 32x32 C tiles (v_max3_f32 chains).
+__device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
+    float x = fmaxf(a[0], a[1]), y = fmaxf(b[0], b[1]);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) {
+        x = fmaxf(fmaxf(x, a[i]), a[i + 1]);
+        y = fmaxf(fmaxf(y, b[i]), b[i + 1]);
+    }
+    return fmaxf(x, y);
+}
+
 // Row (key or query) held by register i of lane half h in a 32x32 C tile.
 __device__ __forceinline__ constexpr int c_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 

@@ -15,12 +15,13 @@
 // Work split (FlashAttention-2's sequence-dimension parallelism, same page):
 // one workgroup of 4 wavefronts per (batch*head, block of 128 query rows);
 // each wavefront owns 32 query rows, so no softmax statistic is ever shared
-// between wavefronts.  Each key tile of 64 keys is staged once in LDS and read
-// by all four wavefronts:
-//   K   row-major  [64 keys][d]   (+8 bf16 padding per row)
-//   V^T transposed [d][64 slots]  (+8 bf16 padding per row), key -> key_slot()
+// between wavefronts.  Each key tile of 64 keys is staged once in LDS, double
+// buffered, and read by all four wavefronts:
+//   K row-major [64 keys][d] -> A operand of S^T = K Q^T (16-byte reads)
+//   V row-major [64 keys][d] -> A operand of O^T = V^T P^T through the gfx950
+//                               transposing read ds_read_b64_tr_b16
 // Global loads for tile j+1 are issued into registers before tile j is
-// computed, so HBM/L2 latency overlaps the MFMA work.
+// computed and land in the other LDS buffer afterwards: one barrier per tile.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -33,180 +34,169 @@ constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kFwdBr = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBc = 64;              // keys per tile
 
-// Map a flat workgroup id to (head, query block).  Consecutive ids walk the
-// heads of one query block, so for causal masks every head's heaviest block
-// (the last one) is dispatched first, and -- because the hardware deals ids
-// round-robin to the 8 XCDs -- all blocks of a head land on the same XCD
-// whenever the head count is a multiple of 8, keeping its K/V in one L2.
-__device__ __forceinline__ void wg_coords(int id, int BH, int nqb, bool causal, int& bh, int& qb) {
-    bh = id % BH;
-    const int qi = id / BH;
+// Map a flat workgroup id to (head, query block): XCD-contiguous task ranges
+// (see xcd_task), head-major, and within a head the heaviest query block (the
+// last, under a causal mask) first.  Returns false for padding workgroups.
+__device__ __forceinline__ bool wg_coords(int id, int BH, int nqb, bool causal, int& bh, int& qb) {
+    const int task = xcd_task(id, BH * nqb);
+    if (task >= BH * nqb) return false;
+    bh = task / nqb;
+    const int qi = task % nqb;
     qb = causal ? (nqb - 1 - qi) : qi;
+    return true;
 }
+
+// Threshold (log2 units) by which a row's maximum must grow before the
+// accumulator is rescaled.  Any reference value m gives the same exact result
+// (O = acc / l and L = m + log2 l both carry it), so m may lag the true maximum:
+// P = 2^(S c - m) then stays below 2^8, comfortably inside fp32 and bf16 range,
+// and most key tiles skip the alpha rescale of the accumulator.
+constexpr float kRescaleThreshold = 8.0f;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, float scale_log2) {
     constexpr int BC = kFwdBc;
-    constexpr int KS = D + 8;   // LDS row stride of K (elements)
-    constexpr int VS = BC + 8;  // LDS row stride of V^T (elements)
+    constexpr int KS = D + 8;   // K row stride: 16 consecutive rows hit distinct banks (b128 reads)
+    constexpr int VS = D + 16;  // V row stride: 4 rows x 32 B transposed reads hit distinct banks
     constexpr int DCH = D / 8;  // 16-byte chunks per row
-    constexpr int KCH = BC * DCH / kFwdThreads;  // K chunks loaded per thread
-    constexpr int VKG = BC * DCH / kFwdThreads;  // keys per V group (4 at d=128, 2 at d=64)
-    static_assert(KCH * kFwdThreads == BC * DCH, "K tile split");
-    static_assert(VKG == 2 || VKG == 4, "V group");
-    constexpr int VDCH_PER_WAVE = DCH / kFwdWaves;  // d chunks handled by one wave for V
+    constexpr int CH = BC * DCH / kFwdThreads;  // chunks per thread per tensor
+    static_assert(CH * kFwdThreads == BC * DCH, "tile split");
 
-    __shared__ __attribute__((aligned(16))) bf16 sK[BC * KS];
-    __shared__ __attribute__((aligned(16))) bf16 sVt[D * VS];
+    __shared__ __attribute__((aligned(16))) bf16 sK[2][BC * KS];
+    __shared__ __attribute__((aligned(16))) bf16 sV[2][BC * VS];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int lq = lane & 31, h = lane >> 5;
     int bh, qb;
-    wg_coords(blockIdx.x, BH, nqb, CAUSAL, bh, qb);
+    if (!wg_coords(blockIdx.x, BH, nqb, CAUSAL, bh, qb)) return;
     const int q0 = qb * kFwdBr;
     const int qw0 = q0 + 32 * w;  // first query row of this wave
     const int qrow = qw0 + lq;    // this lane's query row
     const int64_t base = (int64_t)bh * N * D;
 
+    // Per-head buffer resources: rows past N read as zero.
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
+
     // Q^T operand: k-step ks holds Q[qrow][16 ks + 8 h .. +7].
     bf16x8 qf[D / 16];
-    {
-        const bf16* qp = Q + base + (int64_t)qrow * D + 8 * h;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            if (qrow < N) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
-            else qf[ks] = bf16x8{};
-        }
-    }
+    for (int ks = 0; ks < D / 16; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(qrs, (lq * D + 16 * ks + 8 * h) * 2, qw0 * D * 2));
 
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-    float m = -INFINITY;  // running max of the scaled (log2-domain) scores
-    float l = 0.f;        // running partial sum of this lane's keys
+    float m = -INFINITY;  // reference maximum of the scaled (log2-domain) scores
+    float l = 0.f;        // running partial sum over this lane's keys
 
     int ntiles = (N + BC - 1) / BC;
     if (CAUSAL) ntiles = min(ntiles, (min(q0 + kFwdBr, N) - 1) / BC + 1);
 
-    // Register staging of the next tile.
-    u32x4 kreg[KCH];
-    u32x4 vreg[VKG];
-    const int vdch = w * VDCH_PER_WAVE + (lane % VDCH_PER_WAVE);
-    const int vkg = lane / VDCH_PER_WAVE;  // group of VKG keys
+    // Register staging of the next tile (row-major copies of K and V).  Thread
+    // chunk r covers row (tid + 256 r) / DCH, 16-byte column tid % DCH; the
+    // tile offset rides in the scalar offset, so the VGPR offset is fixed.
+    u32x4 kreg[CH], vreg[CH];
+    constexpr int ROWS_PER_PASS = kFwdThreads / DCH;
+    const int ld_off = ((tid / DCH) * D + 8 * (tid % DCH)) * 2;
     auto load_tile = [&](int j) {
-        const int k0 = j * BC;
+        const int soff = j * BC * D * 2;
 #pragma unroll
-        for (int r = 0; r < KCH; ++r) {
-            const int c = tid + kFwdThreads * r;
-            const int key = k0 + c / DCH, dch = c % DCH;
-            kreg[r] = key < N ? *reinterpret_cast<const u32x4*>(K + base + (int64_t)key * D + 8 * dch)
-                              : u32x4{};
-        }
-#pragma unroll
-        for (int kk = 0; kk < VKG; ++kk) {
-            const int key = k0 + vkg * VKG + kk;
-            vreg[kk] = key < N ? *reinterpret_cast<const u32x4*>(V + base + (int64_t)key * D + 8 * vdch)
-                               : u32x4{};
+        for (int r = 0; r < CH; ++r) {
+            kreg[r] = buffer_load16(krs, ld_off + r * ROWS_PER_PASS * D * 2, soff);
+            vreg[r] = buffer_load16(vrs, ld_off + r * ROWS_PER_PASS * D * 2, soff);
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int r = 0; r < KCH; ++r) {
+        for (int r = 0; r < CH; ++r) {
             const int c = tid + kFwdThreads * r;
-            *reinterpret_cast<u32x4*>(&sK[(c / DCH) * KS + 8 * (c % DCH)]) = kreg[r];
-        }
-        // Transpose VKG keys x 8 dims in registers: one store per dim.
-        const int slot0 = key_slot(vkg * VKG);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            uint16_t e[VKG];
-#pragma unroll
-            for (int kk = 0; kk < VKG; ++kk) e[kk] = (uint16_t)(vreg[kk][t >> 1] >> (16 * (t & 1)));
-            bf16* dst = &sVt[(8 * vdch + t) * VS + slot0];
-            if constexpr (VKG == 4) {
-                *reinterpret_cast<u32x2*>(dst) =
-                    u32x2{(uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16)};
-            } else {
-                *reinterpret_cast<uint32_t*>(dst) = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
-            }
+            *reinterpret_cast<u32x4*>(&sK[buf][(c / DCH) * KS + 8 * (c % DCH)]) = kreg[r];
+            *reinterpret_cast<u32x4*>(&sV[buf][(c / DCH) * VS + 8 * (c % DCH)]) = vreg[r];
         }
     };
 
-    if (ntiles > 0) load_tile(0);
+    // Per-lane offsets of the K rows (b128 reads) and the transposed V reads.
+    const int k_off = lq * KS + 8 * h;
+    const int v_off = tr_row(lane) * VS + tr_col(lane);
+
+    // Loads and stores are unconditional (the last iteration re-reads the final
+    // tile into the idle buffer): every path then drains the load counter at the
+    // store, so the compiler never makes the math wait on a pending load.
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
-        __syncthreads();  // every wave is done reading the previous tile
-        store_tile();
-        __syncthreads();
-        if (j + 1 < ntiles) load_tile(j + 1);
+        const int buf = j & 1;
+        load_tile(min(j + 1, ntiles - 1));  // in flight during this tile's math
 
         const int k0 = j * BC;
-        if (CAUSAL && k0 > qw0 + 31) continue;  // tile entirely above this wave's diagonal
-
-        // S^T = K Q^T for two 32-key halves.
-        f32x16 s[2];
+        // Skip tiles entirely above this wave's diagonal (a scalar branch).
+        if (!CAUSAL || __builtin_amdgcn_readfirstlane(k0 <= qw0 + 31)) {
+            const bf16* kt = sK[buf];
+            const bf16* vt = sV[buf];
+            // S^T = K Q^T for two 32-key halves.
+            f32x16 s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = f32x16{};
-            const bf16* kp = &sK[(32 * kb + lq) * KS + 8 * h];
+            for (int kb = 0; kb < 2; ++kb) {
+                s[kb] = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks)
-                s[kb] = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(kp + 16 * ks), qf[ks], s[kb]);
-        }
+                for (int ks = 0; ks < D / 16; ++ks)
+                    s[kb] = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(kt + 32 * kb * KS + k_off + 16 * ks),
+                                               qf[ks], s[kb]);
+            }
 
-        // Mask keys past N and, on tiles crossing the diagonal, keys after the query.
-        const bool ragged = k0 + BC > N;
-        const bool diag = CAUSAL && (k0 + BC - 1 > qw0);
-        if (ragged || diag) {
+            // Mask keys past N and, on tiles crossing the diagonal, keys after the query.
+            if (k0 + BC > N || (CAUSAL && k0 + BC - 1 > qw0)) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = k0 + 32 * kb + c_row(i, h);
+                        if (key >= N || (CAUSAL && key > qrow)) s[kb][i] = -INFINITY;
+                    }
+            }
+
+            // Online softmax in the log2 domain with a lagging reference max.
+            const float mx = pair_max(max32(s[0], s[1])) * scale_log2;
+            if (__any(mx > m + kRescaleThreshold)) {  // wave-uniform branch
+                const float m_new = fmaxf(m, mx);
+                const float alpha = fast_exp2(m - m_new);  // 0 on the first visible tile
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+                m = m_new;
+            }
+            const float m_use = (m == -INFINITY) ? 0.f : m;  // row with nothing visible yet
+            float rs0 = 0.f, rs1 = 0.f;
+            bf16x8 pf[BC / 16];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int key = k0 + 32 * kb + c_row(i, h);
-                    if (key >= N || (CAUSAL && key > qrow)) s[kb][i] = -INFINITY;
+                    const float p = fast_exp2(fmaf(s[kb][i], scale_log2, -m_use));
+                    if (i & 1) rs1 += p;
+                    else rs0 += p;
+                    // k-step s2 = 2 kb + i/8 covers keys 16 s2 + 8 (j/4) + 4 h + j%4, j = i%8
+                    pf[2 * kb + (i >> 3)][i & 7] = (bf16)p;
                 }
+            l += rs0 + rs1;
+
+            // O^T += V^T P^T, V^T read transposed from the row-major V tile.
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int s2 = 0; s2 < BC / 16; ++s2)
+                    oacc[db] = mfma_bf16_32x32x16(lds_read_tr_a(vt + 16 * s2 * VS + v_off + 32 * db, VS), pf[s2],
+                                                  oacc[db]);
         }
 
-        // Online softmax in the log2 domain.
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = pair_max(mx);
-        const float m_new = fmaxf(m, mx * scale_log2);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // fully masked so far
-        const float alpha = fast_exp2(m - m_use);
-        m = m_new;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(fmaf(s[kb][i], scale_log2, -m_use));
-                s[kb][i] = p;
-                rs += p;
-            }
-        l = fmaf(l, alpha, rs);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-
-        // P^T operands (bf16), k-step s2 covers keys 16 s2 .. 16 s2 + 15.
-        bf16x8 pf[BC / 16];
-#pragma unroll
-        for (int s2 = 0; s2 < BC / 16; ++s2)
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj) pf[s2][jj] = (bf16)s[s2 >> 1][8 * (s2 & 1) + jj];
-
-        // O^T += V^T P^T.
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const bf16* vp = &sVt[(32 * db + lq) * VS + 8 * h];
-#pragma unroll
-            for (int s2 = 0; s2 < BC / 16; ++s2)
-                oacc[db] = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(vp + 16 * s2), pf[s2], oacc[db]);
-        }
+        store_tile(buf ^ 1);  // buffer last read in the previous tile
+        __syncthreads();
     }
 
     // Epilogue: O = acc / l, L = (m + log2 l) ln 2.
@@ -246,7 +236,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_f32_kernel(
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lq = lane & 31, h = lane >> 5;
     int bh, qb;
-    wg_coords(blockIdx.x, BH, nqb, CAUSAL, bh, qb);
+    if (!wg_coords(blockIdx.x, BH, nqb, CAUSAL, bh, qb)) return;
     const int q0 = qb * kFwdBr;
     const int qw0 = q0 + 32 * w;
     const int qrow = qw0 + lq;
@@ -356,7 +346,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_f32_kernel(
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                            int N, int d, float scale, bool causal, hipStream_t stream) {
     const int nqb = (N + kFwdBr - 1) / kFwdBr;
-    const int grid = nqb * BH;
+    const int grid = grid_for_tasks(nqb * BH);
     const float sl2 = scale * kLog2e;
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
@@ -380,7 +370,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
                           int N, int d, float scale, bool causal, hipStream_t stream) {
     const int nqb = (N + kFwdBr - 1) / kFwdBr;
-    const int grid = nqb * BH;
+    const int grid = grid_for_tasks(nqb * BH);
     const float sl2 = scale * kLog2e;
 #define FA_FWD_LAUNCH(DD, CC)                                                                        \
     do {                                                                                             \
