@@ -9,10 +9,12 @@
 //
 // Three kernels run in stream order:
 //   1. preprocess   D_i = sum_t dO_it O_it                    (bandwidth-bound)
-//   2. dK/dV        one workgroup per 128 keys (32 per wavefront), walking the
-//                   query blocks; the wavefront's K and V rows stay in
-//                   registers as MFMA operands, dK and dV accumulate in
-//                   registers and are written once.
+//   2. dV, dK       two kernels, one workgroup per 128 keys (32 per
+//                   wavefront), walking the query blocks; the wavefront's K (and
+//                   V) rows stay in registers as MFMA operands, and dV (or dK)
+//                   accumulates in registers and is written once.  Splitting
+//                   them recomputes S once more but halves the accumulator
+//                   registers, so two wavefronts share each SIMD.
 //   3. dQ           one workgroup per 128 query rows (32 per wavefront),
 //                   walking the key tiles; dQ accumulates in registers.
 // Tiles are staged row-major in double-buffered LDS through buffer loads (rows
@@ -93,23 +95,25 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_preprocess_kernel(const bf16*
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK, dV.  Per block of 64 query rows, staged row-major in LDS (double
-//    buffered): Q, dO, L (log2 domain, +inf past N) and D.
-//    Per wavefront (32 keys) and 32-query half, with C tiles [query x key]:
+// 2. dK and dV, as two kernels of one template (each holds one fp32
+//    accumulator, so two wavefronts fit per SIMD).  Per block of 64 query rows,
+//    staged row-major in LDS (double buffered): Q, dO, and L (log2 domain, +inf
+//    past N) and D.  Per wavefront (32 keys) and 32-query half, with C tiles
+//    [query x key]:
 //      S  = Q K^T            (A = Q rows from LDS, B = K^T from registers)
-//      dP = dO V^T           (A = dO rows from LDS, B = V^T from registers)
-//      P  = exp2(S c - L2), dS = P (dP - D)
-//      dV^T += dO^T P        (A = dO^T: transposing LDS reads; B = P from registers)
-//      dK^T += Q^T dS        (A = Q^T:  transposing LDS reads; B = dS from registers)
+//      P  = exp2(S c - L2)
+//      dV: dV^T += dO^T P    (A = dO^T: transposing LDS reads; B = P)
+//      dK: dP = dO V^T       (A = dO rows from LDS, B = V^T from registers)
+//          dS = P (dP - D);  dK^T += Q^T dS  (A = Q^T: transposing reads; B = dS)
 
 constexpr int kDkvBq = 64;    // query rows per step
 constexpr int kDkvBkv = 128;  // keys per workgroup
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
+template <int D, bool CAUSAL, bool DK>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    float* __restrict__ dK, float* __restrict__ dV, int N, int BH, int nkb, float scale_log2, float scale) {
+    float* __restrict__ dOut, int N, int BH, int nkb, float scale_log2, float out_scale) {
     constexpr int BQ = kDkvBq;
     constexpr int RS = both_ways_stride<D>();
     __shared__ __attribute__((aligned(16))) bf16 sQ[2][BQ * RS];
@@ -134,23 +138,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
     const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + base, head_bytes);
 
-    // K^T and V^T operands of this lane's key (zero past N).
-    bf16x8 kf[D / 16], vf[D / 16];
+    // K^T (and, for dK, V^T) operands of this lane's key (zero past N).
+    bf16x8 kf[D / 16], vf[DK ? D / 16 : 1];
     {
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             kf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(krs, (lq * D + 16 * ks + 8 * h) * 2, kw0 * D * 2));
-            vf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(vrs, (lq * D + 16 * ks + 8 * h) * 2, kw0 * D * 2));
+            if constexpr (DK)
+                vf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(vrs, (lq * D + 16 * ks + 8 * h) * 2, kw0 * D * 2));
         }
     }
-    f32x16 dkacc[D / 32], dvacc[D / 32];
+    f32x16 acc[D / 32];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        dkacc[db] = f32x16{};
-        dvacc[db] = f32x16{};
-    }
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
     const int nqblk = (N + BQ - 1) / BQ;
     const int iq0 = CAUSAL ? k0 / BQ : 0;
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
         if (tid < BQ) {
             const int r = min(i0 + tid, N - 1);
             lreg = i0 + tid < N ? lse_h[r] * kLog2e : INFINITY;  // P = 0 past N
-            dreg = i0 + tid < N ? d_h[r] : 0.f;
+            if constexpr (DK) dreg = i0 + tid < N ? d_h[r] : 0.f;
         }
     };
     auto store_block = [&](int buf) {
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
         stg.store(sdO[buf], RS);
         if (tid < BQ) {
             sL[buf][tid] = lreg;
-            sD[buf][tid] = dreg;
+            if constexpr (DK) sD[buf][tid] = dreg;
         }
     };
     // Per-lane LDS offsets: 16-byte rows and transposing reads.
@@ -203,33 +205,33 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
                 for (int ks = 0; ks < D / 16; ++ks) {
                     s = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(qt + 32 * qh * RS + row_off + 16 * ks),
                                            kf[ks], s);
-                    dp = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(gt + 32 * qh * RS + row_off + 16 * ks),
-                                            vf[ks], dp);
+                    if constexpr (DK)
+                        dp = mfma_bf16_32x32x16(
+                            *reinterpret_cast<const bf16x8*>(gt + 32 * qh * RS + row_off + 16 * ks), vf[ks], dp);
                 }
                 // Register i holds query 32 qh + c_row(i, h); four consecutive queries per float4.
-                bf16x8 pf[2], dsf[2];
+                bf16x8 bop[2];  // P (dV) or dS (dK), the B operand of the k-steps
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][32 * qh + 8 * r + 4 * h]);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[buf][32 * qh + 8 * r + 4 * h]);
+                    f32x4 d4 = f32x4{};
+                    if constexpr (DK) d4 = *reinterpret_cast<const f32x4*>(&sD[buf][32 * qh + 8 * r + 4 * h]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int i = 4 * r + e;
                         float p = fast_exp2(fmaf(s[i], scale_log2, -l4[e]));
                         if (diag && key > i0 + 32 * qh + c_row(i, h)) p = 0.f;
-                        pf[i >> 3][i & 7] = (bf16)p;
-                        dsf[i >> 3][i & 7] = (bf16)(p * (dp[i] - d4[e]));
+                        bop[i >> 3][i & 7] = (bf16)(DK ? p * (dp[i] - d4[e]) : p);
                     }
                 }
                 // k-step s2 covers queries 32 qh + 16 s2 + {4h + e, 8 + 4h + e}.
+                const bf16* at = DK ? qt : gt;  // A = Q^T (dK) or dO^T (dV)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const int off = (32 * qh + 16 * s2) * RS + tr_off;
 #pragma unroll
-                    for (int db = 0; db < D / 32; ++db) {
-                        dvacc[db] = mfma_bf16_32x32x16(lds_read_tr_a(gt + off + 32 * db, RS), pf[s2], dvacc[db]);
-                        dkacc[db] = mfma_bf16_32x32x16(lds_read_tr_a(qt + off + 32 * db, RS), dsf[s2], dkacc[db]);
-                    }
+                    for (int db = 0; db < D / 32; ++db)
+                        acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(at + off + 32 * db, RS), bop[s2], acc[db]);
                 }
             }
         }
@@ -239,18 +241,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
 
     // Register i of block db holds dim 32 db + c_row(i, h) of this lane's key.
     if (key < N) {
-        float* dkp = dK + base + (int64_t)key * D + 4 * h;
-        float* dvp = dV + base + (int64_t)key * D + 4 * h;
+        float* op = dOut + base + (int64_t)key * D + 4 * h;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                *reinterpret_cast<f32x4*>(dkp + 32 * db + 8 * r) =
-                    f32x4{dkacc[db][4 * r] * scale, dkacc[db][4 * r + 1] * scale, dkacc[db][4 * r + 2] * scale,
-                          dkacc[db][4 * r + 3] * scale};
-                *reinterpret_cast<f32x4*>(dvp + 32 * db + 8 * r) =
-                    f32x4{dvacc[db][4 * r], dvacc[db][4 * r + 1], dvacc[db][4 * r + 2], dvacc[db][4 * r + 3]};
-            }
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<f32x4*>(op + 32 * db + 8 * r) =
+                    f32x4{acc[db][4 * r] * out_scale, acc[db][4 * r + 1] * out_scale, acc[db][4 * r + 2] * out_scale,
+                          acc[db][4 * r + 3] * out_scale};
     }
 }
 
@@ -393,8 +391,13 @@ hipError_t launch_dkdv_t(const bf16* q, const bf16* k, const bf16* v, const floa
                          const float* delta, float* dk, float* dv, int BH, int N, float scale,
                          hipStream_t stream) {
     const int nkb = (N + kDkvBkv - 1) / kDkvBkv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(grid_for_tasks(nkb * BH)), dim3(kBwdThreads), 0, stream, q, k, v,
-                       dout, lse, delta, dk, dv, N, BH, nkb, scale * kLog2e, scale);
+    const int grid = grid_for_tasks(nkb * BH);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3(grid), dim3(kBwdThreads), 0, stream, q, k, v, dout,
+                       lse, delta, dv, N, BH, nkb, scale * kLog2e, 1.0f);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3(grid), dim3(kBwdThreads), 0, stream, q, k, v, dout,
+                       lse, delta, dk, N, BH, nkb, scale * kLog2e, scale);
     return hipGetLastError();
 }
 
