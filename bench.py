@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark: exact tiled attention forward + backward on one MI355X.
 
-One step = the whole path on one batch: fa_fwd, then the backward's three
-stages (fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq), on synthetic bf16 inputs
+One step = the whole path on one batch: fa_fwd, then the backward's four
+stages (fa_bwd_preprocess, fa_bwd_dv, fa_bwd_dk, fa_bwd_dq), on synthetic bf16 inputs
 already resident in HBM.  Default workload: causal, B=2, H=32, N=8192, d=128
 (the shape the targets are stated at), Q/K/V/dO i.i.d. N(0,1).
 
@@ -25,6 +25,9 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 FLOP/clk)
 PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ("io_aware_tiled_fwd_amd/csrc/fa_fwd.hip", "io_aware_tiled_fwd_amd/csrc/fa_bwd.hip",
+                  "io_aware_tiled_fwd_amd/csrc/fa_common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_causal_b2_h32_n8192_d128.json")
 
 WORKLOADS = {
     # name: (B, H, N, d, causal)
@@ -44,10 +47,10 @@ def counted_flops(B, H, N, d, causal):
 def kernel_flops(B, H, N, d, causal):
     """Algorithmic MFMA FLOPs of each kernel per launch: every visible
     (query, key) pair costs 2 d per matrix product the kernel performs
-    (fwd: S, PV; dK/dV: S, dP, dV, dK; dQ: S, dP, dQ)."""
+    (fwd: S, PV; dV: S, dV; dK: S, dP, dK; dQ: S, dP, dQ)."""
     pairs = N * N * B * H * (0.5 if causal else 1.0)
-    return {"fwd": 2 * 2 * d * pairs, "bwd_dkdv": 4 * 2 * d * pairs, "bwd_dq": 3 * 2 * d * pairs,
-            "bwd_preprocess": 2.0 * N * d * B * H}
+    return {"fwd": 2 * 2 * d * pairs, "bwd_dv": 2 * 2 * d * pairs, "bwd_dk": 3 * 2 * d * pairs,
+            "bwd_dq": 3 * 2 * d * pairs, "bwd_preprocess": 2.0 * N * d * B * H}
 
 
 def kernel_bytes(B, H, N, d):
@@ -55,8 +58,45 @@ def kernel_bytes(B, H, N, d):
     t = 2.0 * B * H * N * d  # one bf16 [B,H,N,d] tensor
     f = 4.0 * B * H * N * d  # one fp32 [B,H,N,d] tensor
     r = 4.0 * B * H * N      # one fp32 [B,H,N] vector
-    return {"fwd": 4 * t + r, "bwd_preprocess": 2 * t + r,
-            "bwd_dkdv": 4 * t + 2 * r + 2 * f, "bwd_dq": 4 * t + 2 * r + f}
+    return {"fwd": 4 * t + r, "bwd_preprocess": 2 * t + r, "bwd_dv": 3 * t + r + f,
+            "bwd_dk": 4 * t + 2 * r + f, "bwd_dq": 4 * t + 2 * r + f}
+
+
+def kernel_source_hash():
+    """sha256 over the kernel sources: a recorded HBM-traffic figure is only
+    reported while the kernels it was measured on are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (scaled by the plain-copy calibration), or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch", {}).get(kernel)
+
+
+def copy_calibration(mib):
+    """A plain device copy of a known size, for calibrating the byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 3}), flush=True)
+    return 0
 
 
 def cpu_baseline(heads, causal):
@@ -90,6 +130,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (counter calibration)")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of batch 0 the CPU baseline computes (about 10-20 s)")
     args = ap.parse_args(argv)
@@ -99,6 +141,9 @@ def main(argv=None):
               "(the forward and backward shard by (batch, head) with no communication).",
               file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
 
     import numpy as np
     import torch
@@ -120,7 +165,7 @@ def main(argv=None):
     dq = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
     dk, dv = torch.empty_like(dq), torch.empty_like(dq)
     stream = torch.cuda.current_stream()
-    names = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+    names = ["fwd", "bwd_preprocess", "bwd_dv", "bwd_dk", "bwd_dq"]
 
     def step(ev=None):
         if ev is not None:
@@ -131,16 +176,19 @@ def main(argv=None):
         binding.fa_bwd_preprocess(o, t["do"], delta, stream)
         if ev is not None:
             ev[2].record(stream)
-        binding.fa_bwd_dkdv(t["q"], t["k"], t["v"], lse, t["do"], delta, dk, dv, causal, scale, stream)
+        binding.fa_bwd_dv(t["q"], t["k"], lse, t["do"], dv, causal, scale, stream)
         if ev is not None:
             ev[3].record(stream)
-        binding.fa_bwd_dq(t["q"], t["k"], t["v"], lse, t["do"], delta, dq, causal, scale, stream)
+        binding.fa_bwd_dk(t["q"], t["k"], t["v"], lse, t["do"], delta, dk, causal, scale, stream)
         if ev is not None:
             ev[4].record(stream)
+        binding.fa_bwd_dq(t["q"], t["k"], t["v"], lse, t["do"], delta, dq, causal, scale, stream)
+        if ev is not None:
+            ev[5].record(stream)
 
     for _ in range(args.warmup):
         step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -158,13 +206,13 @@ def main(argv=None):
     ms_step = wall / args.steps * 1e3
     ff, fb = counted_flops(B, H, N, d, causal)
     value = (ff + fb) / (ms_step / 1e3) / 1e12
-    bwd_ms = med["bwd_preprocess"] + med["bwd_dkdv"] + med["bwd_dq"]
+    bwd_ms = sum(med[n] for n in names if n.startswith("bwd_"))
     kflops = kernel_flops(B, H, N, d, causal)
     kbytes = kernel_bytes(B, H, N, d)
     kernels = {n: {"ms_median": round(med[n], 4), "ms_mean": round(avg[n], 4),
                    "tflops": round(kflops[n] / (avg[n] / 1e3) / 1e12, 2),
                    "gbs_compulsory": round(kbytes[n] / (avg[n] / 1e3) / 1e9, 1)} for n in names}
-    dominant = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: avg[n])
+    dominant = max(("fwd", "bwd_dv", "bwd_dk", "bwd_dq"), key=lambda n: avg[n])
     achieved = kflops[dominant] / (avg[dominant] / 1e3) / 1e12
 
     out = {
@@ -192,7 +240,8 @@ def main(argv=None):
         "kernels": kernels,
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(dominant, args.workload)},
         "peak_bf16_tflops": PEAK_BF16_TFLOPS,
     }
     if not args.no_cpu_baseline:

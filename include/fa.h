@@ -95,19 +95,22 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /*
- * The three stages of fa_bwd, for callers that schedule or time them
+ * The four stages of fa_bwd, for callers that schedule or time them
  * separately.  Calling them in this order on one stream is exactly fa_bwd.
  *
  * fa_bwd_preprocess: delta[i] = sum_t dO_it * O_it (fp32), o and dO bf16.
- * fa_bwd_dkdv:       dK and dV (fp32) from q, k, v, dO (bf16), lse, delta.
- * fa_bwd_dq:         dQ (fp32) from q, k, v, dO (bf16), lse, delta.
+ * fa_bwd_dv:         dV (fp32) from q, k, dO (bf16) and lse.
+ * fa_bwd_dk:         dK (fp32) from q, k, v, dO (bf16), lse and delta.
+ * fa_bwd_dq:         dQ (fp32) from q, k, v, dO (bf16), lse and delta.
  * Arguments have the meaning, layout and checks of fa_bwd.
  */
 int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H, int N, int d,
                       hipStream_t stream);
-int fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO,
-                const float* delta, float* dk, float* dv, int B, int H, int N, int d, float scale,
-                int causal, hipStream_t stream);
+int fa_bwd_dv(const void* q, const void* k, const float* lse, const void* dO, float* dv,
+              int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+int fa_bwd_dk(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+              const float* delta, float* dk, int B, int H, int N, int d, float scale, int causal,
+              hipStream_t stream);
 int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO,
               const float* delta, float* dq, int B, int H, int N, int d, float scale, int causal,
               hipStream_t stream);

@@ -21,8 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
-           "fa_status_string")
+SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dv", "fa_bwd_dk",
+           "fa_bwd_dq", "fa_status_string")
 
 
 class FaError(RuntimeError):
@@ -49,10 +49,11 @@ def load_library():
     lib.fa_fwd_f32.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_preprocess.argtypes = [vp] * 3 + [i, i, i, i, vp]
-    lib.fa_bwd_dkdv.argtypes = [vp] * 8 + [i, i, i, i, f, i, vp]
+    lib.fa_bwd_dv.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
+    lib.fa_bwd_dk.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dq.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
-    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_bwd, lib.fa_bwd_preprocess, lib.fa_bwd_dkdv,
-               lib.fa_bwd_dq):
+    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_bwd, lib.fa_bwd_preprocess, lib.fa_bwd_dv,
+               lib.fa_bwd_dk, lib.fa_bwd_dq):
         fn.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -185,15 +186,35 @@ def fa_bwd_preprocess(o, dout, delta, stream=None) -> None:
         raise FaError(st, "fa_bwd_preprocess")
 
 
-def fa_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, causal=False, scale=None, stream=None) -> None:
-    """dK, dV (fp32) given lse and delta."""
-    B, H, N, d = _check_bwd_args(q, k, v, dout, lse, delta, ((dk, "dk"), (dv, "dv")))
+def fa_bwd_dv(q, k, lse, dout, dv, causal=False, scale=None, stream=None) -> None:
+    """dV (fp32) given lse."""
+    B, H, N, d = _shape(q)
+    for t, n in ((q, "q"), (k, "k"), (dout, "dout")):
+        _check4(t, n, torch.bfloat16)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{n} must have shape {(B, H, N, d)}")
+    _check4(dv, "dv", torch.float32)
+    if tuple(dv.shape) != (B, H, N, d):
+        raise ValueError(f"dv must have shape {(B, H, N, d)}")
+    _check4(lse, "lse", torch.float32)
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"lse must have shape {(B, H, N)}")
     sc = _default_scale(d) if scale is None else float(scale)
-    st = load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta),
-                                    _ptr(dk), _ptr(dv), B, H, N, d, sc, int(bool(causal)),
-                                    ctypes.c_void_p(_stream_handle(stream)))
+    st = load_library().fa_bwd_dv(_ptr(q), _ptr(k), _ptr(lse), _ptr(dout), _ptr(dv), B, H, N, d, sc,
+                                  int(bool(causal)), ctypes.c_void_p(_stream_handle(stream)))
     if st != FA_OK:
-        raise FaError(st, "fa_bwd_dkdv")
+        raise FaError(st, "fa_bwd_dv")
+
+
+def fa_bwd_dk(q, k, v, lse, dout, delta, dk, causal=False, scale=None, stream=None) -> None:
+    """dK (fp32) given lse and delta."""
+    B, H, N, d = _check_bwd_args(q, k, v, dout, lse, delta, ((dk, "dk"),))
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_bwd_dk(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta),
+                                  _ptr(dk), B, H, N, d, sc, int(bool(causal)),
+                                  ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dk")
 
 
 def fa_bwd_dq(q, k, v, lse, dout, delta, dq, causal=False, scale=None, stream=None) -> None:

@@ -76,16 +76,26 @@ int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H,
     return from_hip(fa::launch_bwd_preprocess(o, dO, delta, B * H, N, d, stream));
 }
 
-int fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO,
-                const float* delta, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
-                hipStream_t stream) {
-    if (!q || !k || !v || !lse || !dO || !delta || !dk || !dv) return FA_ERR_INVALID_ARG;
+int fa_bwd_dv(const void* q, const void* k, const float* lse, const void* dO, float* dv, int B, int H, int N, int d,
+              float scale, int causal, hipStream_t stream) {
+    if (!q || !k || !lse || !dO || !dv) return FA_ERR_INVALID_ARG;
     const int st = check_shape(B, H, N, d, scale);
     if (st != FA_OK) return st;
-    const void* ptrs[] = {q, k, v, lse, dO, delta, dk, dv};
+    const void* ptrs[] = {q, k, lse, dO, dv};
     for (const void* p : ptrs)
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
-    return from_hip(fa::launch_bwd_dkdv(q, k, v, lse, dO, delta, dk, dv, B * H, N, d, scale, causal != 0, stream));
+    return from_hip(fa::launch_bwd_dv(q, k, lse, dO, dv, B * H, N, d, scale, causal != 0, stream));
+}
+
+int fa_bwd_dk(const void* q, const void* k, const void* v, const float* lse, const void* dO, const float* delta,
+              float* dk, int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
+    if (!q || !k || !v || !lse || !dO || !delta || !dk) return FA_ERR_INVALID_ARG;
+    const int st = check_shape(B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    const void* ptrs[] = {q, k, v, lse, dO, delta, dk};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+    return from_hip(fa::launch_bwd_dk(q, k, v, lse, dO, delta, dk, B * H, N, d, scale, causal != 0, stream));
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO, const float* delta,

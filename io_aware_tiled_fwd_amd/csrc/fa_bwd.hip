@@ -386,18 +386,12 @@ hipError_t launch_pre_t(const bf16* o, const bf16* dout, float* delta, int BH, i
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DK>
 hipError_t launch_dkdv_t(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
-                         const float* delta, float* dk, float* dv, int BH, int N, float scale,
-                         hipStream_t stream) {
+                         const float* delta, float* out, int BH, int N, float scale, hipStream_t stream) {
     const int nkb = (N + kDkvBkv - 1) / kDkvBkv;
-    const int grid = grid_for_tasks(nkb * BH);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3(grid), dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                       lse, delta, dv, N, BH, nkb, scale * kLog2e, 1.0f);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3(grid), dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                       lse, delta, dk, N, BH, nkb, scale * kLog2e, scale);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK>), dim3(grid_for_tasks(nkb * BH)), dim3(kBwdThreads), 0, stream,
+                       q, k, v, dout, lse, delta, out, N, BH, nkb, scale * kLog2e, DK ? scale : 1.0f);
     return hipGetLastError();
 }
 
@@ -419,18 +413,30 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, 
     return d == 64 ? launch_pre_t<64>(Op, G, delta, BH, N, stream) : launch_pre_t<128>(Op, G, delta, BH, N, stream);
 }
 
-hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                           const float* delta, float* dk, float* dv, int BH, int N, int d, float scale,
-                           bool causal, hipStream_t stream) {
+hipError_t launch_bwd_dv(const void* q, const void* k, const float* lse, const void* dout, float* dv, int BH,
+                         int N, int d, float scale, bool causal, hipStream_t stream) {
+    auto Q = static_cast<const bf16*>(q);
+    auto K = static_cast<const bf16*>(k);
+    auto G = static_cast<const bf16*>(dout);
+    if (d == 64)
+        return causal ? launch_dkdv_t<64, true, false>(Q, K, K, lse, G, nullptr, dv, BH, N, scale, stream)
+                      : launch_dkdv_t<64, false, false>(Q, K, K, lse, G, nullptr, dv, BH, N, scale, stream);
+    return causal ? launch_dkdv_t<128, true, false>(Q, K, K, lse, G, nullptr, dv, BH, N, scale, stream)
+                  : launch_dkdv_t<128, false, false>(Q, K, K, lse, G, nullptr, dv, BH, N, scale, stream);
+}
+
+hipError_t launch_bwd_dk(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                         const float* delta, float* dk, int BH, int N, int d, float scale, bool causal,
+                         hipStream_t stream) {
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
     auto V = static_cast<const bf16*>(v);
     auto G = static_cast<const bf16*>(dout);
     if (d == 64)
-        return causal ? launch_dkdv_t<64, true>(Q, K, V, lse, G, delta, dk, dv, BH, N, scale, stream)
-                      : launch_dkdv_t<64, false>(Q, K, V, lse, G, delta, dk, dv, BH, N, scale, stream);
-    return causal ? launch_dkdv_t<128, true>(Q, K, V, lse, G, delta, dk, dv, BH, N, scale, stream)
-                  : launch_dkdv_t<128, false>(Q, K, V, lse, G, delta, dk, dv, BH, N, scale, stream);
+        return causal ? launch_dkdv_t<64, true, true>(Q, K, V, lse, G, delta, dk, BH, N, scale, stream)
+                      : launch_dkdv_t<64, false, true>(Q, K, V, lse, G, delta, dk, BH, N, scale, stream);
+    return causal ? launch_dkdv_t<128, true, true>(Q, K, V, lse, G, delta, dk, BH, N, scale, stream)
+                  : launch_dkdv_t<128, false, true>(Q, K, V, lse, G, delta, dk, BH, N, scale, stream);
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
@@ -452,7 +458,9 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            int d, float scale, bool causal, hipStream_t stream) {
     hipError_t e = launch_bwd_preprocess(o, dout, delta, BH, N, d, stream);
     if (e != hipSuccess) return e;
-    e = launch_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, BH, N, d, scale, causal, stream);
+    e = launch_bwd_dv(q, k, lse, dout, dv, BH, N, d, scale, causal, stream);
+    if (e != hipSuccess) return e;
+    e = launch_bwd_dk(q, k, v, lse, dout, delta, dk, BH, N, d, scale, causal, stream);
     if (e != hipSuccess) return e;
     return launch_bwd_dq(q, k, v, lse, dout, delta, dq, BH, N, d, scale, causal, stream);
 }

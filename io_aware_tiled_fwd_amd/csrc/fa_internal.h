@@ -18,9 +18,11 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
 // The backward's stages, individually.
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int BH, int N, int d,
                                  hipStream_t stream);
-hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                           const float* delta, float* dk, float* dv, int BH, int N, int d, float scale,
-                           bool causal, hipStream_t stream);
+hipError_t launch_bwd_dv(const void* q, const void* k, const float* lse, const void* dout, float* dv, int BH,
+                         int N, int d, float scale, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dk(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                         const float* delta, float* dk, int BH, int N, int d, float scale, bool causal,
+                         hipStream_t stream);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                          const float* delta, float* dq, int BH, int N, int d, float scale, bool causal,
                          hipStream_t stream);

@@ -310,3 +310,21 @@ def test_abi_errors_leave_outputs_untouched():
     with pytest.raises(binding.FaError):
         binding.fa_fwd(q[:, :, :, :96].contiguous(), q[:, :, :, :96].contiguous(),
                        q[:, :, :, :96].contiguous(), o[:, :, :, :96].contiguous(), lse)
+
+
+def test_backward_stages_equal_fa_bwd():
+    """fa_bwd_preprocess, fa_bwd_dv, fa_bwd_dk, fa_bwd_dq in stream order are fa_bwd."""
+    for causal in (False, True):
+        ts = inputs.normal_qkv(1, 3, 777, 128, 71, with_dout=True)
+        dev = upload(ts)
+        o, lse = _fwd(dev, causal, None)
+        dq, dk, dv = binding.attention_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], causal=causal)
+        delta = torch.empty_like(lse)
+        sq, sk, sv = (torch.full_like(dq, float("nan")) for _ in range(3))
+        binding.fa_bwd_preprocess(o, dev["do"], delta)
+        binding.fa_bwd_dv(dev["q"], dev["k"], lse, dev["do"], sv, causal)
+        binding.fa_bwd_dk(dev["q"], dev["k"], dev["v"], lse, dev["do"], delta, sk, causal)
+        binding.fa_bwd_dq(dev["q"], dev["k"], dev["v"], lse, dev["do"], delta, sq, causal)
+        torch.cuda.synchronize()
+        for a, b in ((sq, dq), (sk, dk), (sv, dv)):
+            assert torch.equal(a, b)
