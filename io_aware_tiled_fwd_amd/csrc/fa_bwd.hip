@@ -26,6 +26,8 @@
 // Causal masks skip (query block, key block) pairs entirely above the diagonal
 // and mask only the pairs that cross it.  Rows past N are staged as zeros, with
 // L = +inf (so P = 0) and D = 0, and are never stored.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -33,7 +35,11 @@ namespace fa {
 
 namespace {
 
-constexpr int kBwdThreads = 256;
+#ifndef FA_BWD_WAVES
+#define FA_BWD_WAVES 8
+#endif
+constexpr int kBwdWaves = FA_BWD_WAVES;
+constexpr int kBwdThreads = 64 * kBwdWaves;
 
 // Row stride (elements) of a bf16 [rows][D] LDS tile that is read both as
 // 16-byte rows (MFMA operand M) and through ds_read_b64_tr_b16 (operand M^T):
@@ -107,10 +113,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_preprocess_kernel(const bf16*
 //          dS = P (dP - D);  dK^T += Q^T dS  (A = Q^T: transposing reads; B = dS)
 
 constexpr int kDkvBq = 64;    // query rows per step
-constexpr int kDkvBkv = 128;  // keys per workgroup
+constexpr int kDkvBkv = 32 * kBwdWaves;  // keys per workgroup
 
 template <int D, bool CAUSAL, bool DK>
-__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     float* __restrict__ dOut, int N, int BH, int nkb, float scale_log2, float out_scale) {
@@ -189,13 +195,16 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
         store_block(0);
     }
     __syncthreads();
-    for (int iq = iq0; iq < nqblk; ++iq) {
+    // One step of 64 query rows.  MASK applies the causal mask; only the steps
+    // whose queries overlap this workgroup's keys (the first two) need it, so
+    // the loop is split and the other steps carry no mask code.
+    auto step = [&](int iq, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int buf = (iq - iq0) & 1;
         load_block(min(iq + 1, nqblk - 1));
         const int i0 = iq * BQ;
         // Skip blocks whose every query precedes every key of this wave.
         if (!CAUSAL || __builtin_amdgcn_readfirstlane(i0 + BQ - 1 >= kw0)) {
-            const bool diag = CAUSAL && __builtin_amdgcn_readfirstlane(i0 < kw0 + 31);
             const bf16* qt = sQ[buf];
             const bf16* gt = sdO[buf];
 #pragma unroll
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
                             *reinterpret_cast<const bf16x8*>(gt + 32 * qh * RS + row_off + 16 * ks), vf[ks], dp);
                 }
                 // Register i holds query 32 qh + c_row(i, h); four consecutive queries per float4.
-                bf16x8 bop[2];  // P (dV) or dS (dK), the B operand of the k-steps
+                float v[16];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][32 * qh + 8 * r + 4 * h]);
@@ -220,24 +229,33 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
                     for (int e = 0; e < 4; ++e) {
                         const int i = 4 * r + e;
                         float p = fast_exp2(fmaf(s[i], scale_log2, -l4[e]));
-                        if (diag && key > i0 + 32 * qh + c_row(i, h)) p = 0.f;
-                        bop[i >> 3][i & 7] = (bf16)(DK ? p * (dp[i] - d4[e]) : p);
+                        if constexpr (MASK) {
+                            if (key > i0 + 32 * qh + c_row(i, h)) p = 0.f;
+                        }
+                        v[i] = DK ? p * (dp[i] - d4[e]) : p;
                     }
                 }
+                // B operand (P for dV, dS for dK) of k-steps 0 and 1.
+                const bf16x8 bop0 = pack_bf16x8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+                const bf16x8 bop1 = pack_bf16x8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
                 // k-step s2 covers queries 32 qh + 16 s2 + {4h + e, 8 + 4h + e}.
                 const bf16* at = DK ? qt : gt;  // A = Q^T (dK) or dO^T (dV)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int off = (32 * qh + 16 * s2) * RS + tr_off;
+                for (int db = 0; db < D / 32; ++db)
+                    acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(at + 32 * qh * RS + tr_off + 32 * db, RS), bop0, acc[db]);
 #pragma unroll
-                    for (int db = 0; db < D / 32; ++db)
-                        acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(at + off + 32 * db, RS), bop[s2], acc[db]);
-                }
+                for (int db = 0; db < D / 32; ++db)
+                    acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(at + (32 * qh + 16) * RS + tr_off + 32 * db, RS), bop1,
+                                                 acc[db]);
             }
         }
         store_block(buf ^ 1);
         __syncthreads();
-    }
+    };
+    // Steps whose query block starts before this workgroup's last key.
+    const int iq_split = CAUSAL ? min(nqblk, (k0 + kDkvBkv - 1) / BQ + 1) : iq0;
+    for (int iq = iq0; iq < iq_split; ++iq) step(iq, std::true_type{});
+    for (int iq = max(iq0, iq_split); iq < nqblk; ++iq) step(iq, std::false_type{});
 
     // Register i of block db holds dim 32 db + c_row(i, h) of this lane's key.
     if (key < N) {
@@ -261,11 +279,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkdv_kernel(
 //      P^T = exp2(S^T c - L2), dS^T = P^T (dP^T - D)
 //      dQ^T += K^T dS^T  (A = K^T: transposing LDS reads; B = dS^T from registers)
 
-constexpr int kDqBq = 128;  // query rows per workgroup
+constexpr int kDqBq = 32 * kBwdWaves;  // query rows per workgroup
 constexpr int kDqBkv = 64;  // keys per step
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     float* __restrict__ dQ, int N, int BH, int nqb, float scale_log2, float scale) {
@@ -320,14 +338,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
     stk.store(sK[0], KS);
     stv.store(sV[0], VS);
     __syncthreads();
-    for (int j = 0; j < ntiles; ++j) {
+    // One key tile.  MASK masks keys past N and (causal) keys after the query;
+    // only the tiles at the diagonal and the ragged end need it, and they come
+    // last, so the loop is split and the other tiles carry no mask code.
+    auto step = [&](int j, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int buf = j & 1;
         const int jn = min(j + 1, ntiles - 1);
         stk.load(krs, jn * BKV);
         stv.load(vrs, jn * BKV);
         const int k0 = j * BKV;
         if (!CAUSAL || __builtin_amdgcn_readfirstlane(k0 <= qw0 + 31)) {
-            const bool mask = __builtin_amdgcn_readfirstlane((k0 + BKV > N) || (CAUSAL && k0 + BKV - 1 > qw0));
             const bf16* kt = sK[buf];
             const bf16* vt = sV[buf];
             bf16x8 dsf[BKV / 16];
@@ -341,15 +362,18 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
                     dp = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(vt + 32 * kh * VS + v_off + 16 * ks),
                                             gf[ks], dp);
                 }
+                float v[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     float p = fast_exp2(fmaf(s[i], scale_log2, -l2));
-                    if (mask) {
+                    if constexpr (MASK) {
                         const int kk = k0 + 32 * kh + c_row(i, h);
                         if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
                     }
-                    dsf[2 * kh + (i >> 3)][i & 7] = (bf16)(p * (dp[i] - dq_d));
+                    v[i] = p * (dp[i] - dq_d);
                 }
+                dsf[2 * kh] = pack_bf16x8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+                dsf[2 * kh + 1] = pack_bf16x8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
             }
             // dQ^T += K^T dS^T; k-step s2 covers keys 16 s2 + {4h + e, 8 + 4h + e}.
 #pragma unroll
@@ -362,7 +386,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(
         stk.store(sK[buf ^ 1], KS);
         stv.store(sV[buf ^ 1], VS);
         __syncthreads();
-    }
+    };
+    // Tiles [j_split, ntiles) reach the diagonal of some wave or the ragged end.
+    const int j_split = CAUSAL ? min(ntiles, q0 / BKV) : (N % BKV ? ntiles - 1 : ntiles);
+    for (int j = 0; j < j_split; ++j) step(j, std::false_type{});
+    for (int j = j_split; j < ntiles; ++j) step(j, std::true_type{});
 
     if (qrow < N) {
         float* dqp = dQ + base + (int64_t)qrow * D + 4 * h;

@@ -103,8 +103,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
     return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
+// soff is made wave-uniform explicitly: an offset the compiler keeps in a VGPR
+// would otherwise put a readfirstlane loop around the load.
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, __builtin_amdgcn_readfirstlane(soff), 0);
+}
+
+// Round eight floats to bf16 (RNE) as four v_cvt_pk_bf16_f32.
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                              float a6, float a7) {
+    const bf16x2 p0 = __builtin_convertvector(f32x2{a0, a1}, bf16x2);
+    const bf16x2 p1 = __builtin_convertvector(f32x2{a2, a3}, bf16x2);
+    const bf16x2 p2 = __builtin_convertvector(f32x2{a4, a5}, bf16x2);
+    const bf16x2 p3 = __builtin_convertvector(f32x2{a6, a7}, bf16x2);
+    return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                            __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)});
 }
 
 // Index of the calling wavefront in its workgroup, as a scalar (wave-uniform)

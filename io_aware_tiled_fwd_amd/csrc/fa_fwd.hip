@@ -13,10 +13,10 @@
 // page, the Triton kernel under "Code").
 //
 // Work split (FlashAttention-2's sequence-dimension parallelism, same page):
-// one workgroup of 4 wavefronts per (batch*head, block of 128 query rows);
+// one workgroup of 8 wavefronts per (batch*head, block of 256 query rows);
 // each wavefront owns 32 query rows, so no softmax statistic is ever shared
 // between wavefronts.  Each key tile of 64 keys is staged once in LDS, double
-// buffered, and read by all four wavefronts:
+// buffered, and read by all eight wavefronts (two per SIMD):
 //   K row-major [64 keys][d] -> A operand of S^T = K Q^T (16-byte reads)
 //   V row-major [64 keys][d] -> A operand of O^T = V^T P^T through the gfx950
 //                               transposing read ds_read_b64_tr_b16
@@ -29,7 +29,7 @@ namespace fa {
 
 namespace {
 
-constexpr int kFwdWaves = 4;
+constexpr int kFwdWaves = 8;
 constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kFwdBr = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBc = 64;              // keys per tile
@@ -54,7 +54,7 @@ __device__ __forceinline__ bool wg_coords(int id, int BH, int nqb, bool causal, 
 constexpr float kRescaleThreshold = 8.0f;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, float scale_log2) {
     constexpr int BC = kFwdBc;
