@@ -17,11 +17,18 @@
 // each wavefront owns 32 query rows, so no softmax statistic is ever shared
 // between wavefronts.  Each key tile of 64 keys is staged once in LDS, double
 // buffered, and read by all eight wavefronts (two per SIMD):
-//   K row-major [64 keys][d] -> A operand of S^T = K Q^T (16-byte reads)
-//   V row-major [64 keys][d] -> A operand of O^T = V^T P^T through the gfx950
-//                               transposing read ds_read_b64_tr_b16
+//   K   row-major [64 keys][d]   -> A operand of S^T = K Q^T
+//   V^T row-major [d][64 keys]   -> A operand of O^T = V^T P^T
+// Both are read as 16-byte rows.  V^T is produced while staging: each wave
+// multiplies a 32-key block of V by identity operands on the MFMA unit
+// (exact: every product is x * 1 or x * 0), which leaves one dimension's keys
+// per lane, and writes them in the key order of the P^T registers (key_slot).
 // Global loads for tile j+1 are issued into registers before tile j is
-// computed and land in the other LDS buffer afterwards: one barrier per tile.
+// computed and land in the other LDS buffers afterwards: one barrier per tile.
+//
+// Latency: the K fragments of S are read four MFMAs ahead, and the V^T
+// fragments of the first two k-steps of O^T are read right after S, so that
+// the exponentials of the softmax run while they arrive.
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -53,19 +60,29 @@ __device__ __forceinline__ bool wg_coords(int id, int BH, int nqb, bool causal, 
 // and most key tiles skip the alpha rescale of the accumulator.
 constexpr float kRescaleThreshold = 8.0f;
 
+// Reads of LDS that must stay where they are written: a volatile access is
+// neither sunk towards its use nor merged, so the data is in flight while the
+// code in between runs.
+__device__ __forceinline__ bf16x8 lds_read16_early(const bf16* p) {
+    return *(const volatile __attribute__((address_space(3))) bf16x8*)(p);
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, float scale_log2) {
     constexpr int BC = kFwdBc;
     constexpr int KS = D + 8;   // K row stride: 16 consecutive rows hit distinct banks (b128 reads)
-    constexpr int VS = D + 16;  // V row stride: 4 rows x 32 B transposed reads hit distinct banks
+    constexpr int VTS = BC + 8;  // V^T row stride, same property
     constexpr int DCH = D / 8;  // 16-byte chunks per row
-    constexpr int CH = BC * DCH / kFwdThreads;  // chunks per thread per tensor
+    constexpr int CH = BC * DCH / kFwdThreads;  // K chunks per thread
     static_assert(CH * kFwdThreads == BC * DCH, "tile split");
+    constexpr int NKS = D / 16;  // k-steps of S
+    constexpr int NDB = D / 32;  // 32-dimension blocks of O
+    constexpr int NPRE = 2;      // k-steps of O^T whose V^T fragments are read early
 
     __shared__ __attribute__((aligned(16))) bf16 sK[2][BC * KS];
-    __shared__ __attribute__((aligned(16))) bf16 sV[2][BC * VS];
+    __shared__ __attribute__((aligned(16))) bf16 sVt[2][D * VTS];
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int lq = lane & 31, h = lane >> 5;
@@ -83,46 +100,72 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
 
     // Q^T operand: k-step ks holds Q[qrow][16 ks + 8 h .. +7].
-    bf16x8 qf[D / 16];
+    bf16x8 qf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+    for (int ks = 0; ks < NKS; ++ks)
         qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(qrs, (lq * D + 16 * ks + 8 * h) * 2, qw0 * D * 2));
 
-    f32x16 oacc[D / 32];
+    f32x16 oacc[NDB];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
     float m = -INFINITY;  // reference maximum of the scaled (log2-domain) scores
     float l = 0.f;        // running partial sum over this lane's keys
 
     int ntiles = (N + BC - 1) / BC;
     if (CAUSAL) ntiles = min(ntiles, (min(q0 + kFwdBr, N) - 1) / BC + 1);
 
-    // Register staging of the next tile (row-major copies of K and V).  Thread
-    // chunk r covers row (tid + 256 r) / DCH, 16-byte column tid % DCH; the
-    // tile offset rides in the scalar offset, so the VGPR offset is fixed.
-    u32x4 kreg[CH], vreg[CH];
+    // Staging of tile j+1 through registers.  K: thread chunk r covers row
+    // (tid + 512 r) / DCH, 16-byte column tid % DCH.  V: the tile is cut into
+    // half-blocks of 32 keys x 16 dimensions, HB consecutive ones per wave; a
+    // lane loads V[32 vkb + lq][16 vd16 + 8 h .. +7] of each, the MFMA operand
+    // A of C = V I.  Tile offsets ride in the scalar offset.
+    constexpr int HB = D / 64;
     constexpr int ROWS_PER_PASS = kFwdThreads / DCH;
     const int ld_off = ((tid / DCH) * D + 8 * (tid % DCH)) * 2;
+    const int vkb = (w * HB) / (D / 16), vd16 = (w * HB) % (D / 16);
+    const int va_off = ((32 * vkb + lq) * D + 16 * vd16 + 8 * h) * 2;
+    // Identity operands: I1[k][n] = (n == k), I2[k][n] = (n == k + 16); lane l holds k = 8 h + j, n = lq.
+    bf16x8 id1, id2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        id1[j] = (bf16)(lq == 8 * h + j ? 1.f : 0.f);
+        id2[j] = (bf16)(lq == 16 + 8 * h + j ? 1.f : 0.f);
+    }
+    u32x4 kreg[CH];
+    bf16x8 va[HB];
     auto load_tile = [&](int j) {
         const int soff = j * BC * D * 2;
 #pragma unroll
-        for (int r = 0; r < CH; ++r) {
-            kreg[r] = buffer_load16(krs, ld_off + r * ROWS_PER_PASS * D * 2, soff);
-            vreg[r] = buffer_load16(vrs, ld_off + r * ROWS_PER_PASS * D * 2, soff);
-        }
+        for (int r = 0; r < CH; ++r) kreg[r] = buffer_load16(krs, ld_off + r * ROWS_PER_PASS * D * 2, soff);
+#pragma unroll
+        for (int t = 0; t < HB; ++t) va[t] = __builtin_bit_cast(bf16x8, buffer_load16(vrs, va_off + 32 * t, soff));
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int r = 0; r < CH; ++r) {
             const int c = tid + kFwdThreads * r;
             *reinterpret_cast<u32x4*>(&sK[buf][(c / DCH) * KS + 8 * (c % DCH)]) = kreg[r];
-            *reinterpret_cast<u32x4*>(&sV[buf][(c / DCH) * VS + 8 * (c % DCH)]) = vreg[r];
+        }
+        // C[key][n] = V[32 vkb + key][16 vd16 + n]: register 4 r + c of lane
+        // (h, lq) holds key 8 r + 4 h + c of dimension 16 vd16 + lq, and keys
+        // 4 apart land in contiguous key slots.
+        f32x16 t = mfma_bf16_32x32x16(va[0], id1, f32x16{});
+        if constexpr (HB == 2) t = mfma_bf16_32x32x16(va[1], id2, t);
+        if (HB == 2 || lq < 16) {
+            bf16* dst = &sVt[buf][(16 * vd16 + lq) * VTS + 32 * vkb + 8 * h];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bf16x2 lo = __builtin_convertvector(f32x2{t[4 * r], t[4 * r + 1]}, bf16x2);
+                const bf16x2 hi = __builtin_convertvector(f32x2{t[4 * r + 2], t[4 * r + 3]}, bf16x2);
+                *reinterpret_cast<u32x2*>(dst + 16 * (r >> 1) + 4 * (r & 1)) =
+                    u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            }
         }
     };
 
-    // Per-lane offsets of the K rows (b128 reads) and the transposed V reads.
+    // Per-lane offsets of the K rows and the V^T rows.
     const int k_off = lq * KS + 8 * h;
-    const int v_off = tr_row(lane) * VS + tr_col(lane);
+    const int v_off = lq * VTS + 8 * h;
 
     // Loads and stores are unconditional (the last iteration re-reads the final
     // tile into the idle buffer): every path then drains the load counter at the
@@ -138,17 +181,32 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
         // Skip tiles entirely above this wave's diagonal (a scalar branch).
         if (!CAUSAL || __builtin_amdgcn_readfirstlane(k0 <= qw0 + 31)) {
             const bf16* kt = sK[buf];
-            const bf16* vt = sV[buf];
-            // S^T = K Q^T for two 32-key halves.
-            f32x16 s[2];
+            const bf16* vt = sVt[buf];
+            if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
+            // S^T = K Q^T for two 32-key halves, the two accumulation chains interleaved.
+            f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = f32x16{};
+            for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks)
+                for (int kb = 0; kb < 2; ++kb)
                     s[kb] = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(kt + 32 * kb * KS + k_off + 16 * ks),
                                                qf[ks], s[kb]);
+            // Issue order: four K reads, then one read per MFMA, so that each
+            // MFMA's operand was requested four MFMAs earlier.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * NKS - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
+
+            bf16x8 vpre[NPRE][NDB];
+#pragma unroll
+            for (int s2 = 0; s2 < NPRE; ++s2)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) vpre[s2][db] = lds_read16_early(vt + 32 * db * VTS + v_off + 16 * s2);
 
             // Mask keys past N and, on tiles crossing the diagonal, keys after the query.
             if (k0 + BC > N || (CAUSAL && k0 + BC - 1 > qw0)) {
@@ -168,7 +226,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
                 const float alpha = fast_exp2(m - m_new);  // 0 on the first visible tile
                 l *= alpha;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+                for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
                 m = m_new;
             }
             const float m_use = (m == -INFINITY) ? 0.f : m;  // row with nothing visible yet
@@ -186,16 +244,20 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
                 }
             l += rs0 + rs1;
 
-            // O^T += V^T P^T, V^T read transposed from the row-major V tile.
+            // O^T += V^T P^T, k-step by k-step.
+            if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+            for (int s2 = 0; s2 < BC / 16; ++s2)
 #pragma unroll
-                for (int s2 = 0; s2 < BC / 16; ++s2)
-                    oacc[db] = mfma_bf16_32x32x16(lds_read_tr_a(vt + 16 * s2 * VS + v_off + 32 * db, VS), pf[s2],
-                                                  oacc[db]);
+                for (int db = 0; db < NDB; ++db) {
+                    const bf16x8 vf = s2 < NPRE ? vpre[s2 < NPRE ? s2 : 0][db]
+                                                : *reinterpret_cast<const bf16x8*>(vt + 32 * db * VTS + v_off + 16 * s2);
+                    oacc[db] = mfma_bf16_32x32x16(vf, pf[s2], oacc[db]);
+                }
+            if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
         }
 
-        store_tile(buf ^ 1);  // buffer last read in the previous tile
+        store_tile(buf ^ 1);  // buffers last read in the previous tile
         __syncthreads();
     }
 
@@ -205,7 +267,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
         const float inv = 1.f / lt;
         bf16* op = O + base + (int64_t)qrow * D + 4 * h;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 bf16x4 o4;
