@@ -210,13 +210,28 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
 #pragma unroll
             for (int qh = 0; qh < BQ / 32; ++qh) {
                 f32x16 s = f32x16{}, dp = f32x16{};
+                if constexpr (DK) {
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    s = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(qt + 32 * qh * RS + row_off + 16 * ks),
-                                           kf[ks], s);
-                    if constexpr (DK)
-                        dp = mfma_bf16_32x32x16(
-                            *reinterpret_cast<const bf16x8*>(gt + 32 * qh * RS + row_off + 16 * ks), vf[ks], dp);
+                    for (int ks = 0; ks < D / 16; ++ks) {
+                        s = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(qt + 32 * qh * RS + row_off + 16 * ks),
+                                               kf[ks], s);
+                        dp = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(gt + 32 * qh * RS + row_off + 16 * ks),
+                                                vf[ks], dp);
+                    }
+                } else {
+                    // dV has registers to spare: each Q fragment is requested four
+                    // MFMAs before its use (volatile reads keep that order).
+                    constexpr int AHEAD = 4;
+                    bf16x8 qa[D / 16];
+#pragma unroll
+                    for (int ks = 0; ks < AHEAD; ++ks)
+                        qa[ks] = lds_read16_early(qt + 32 * qh * RS + row_off + 16 * ks);
+#pragma unroll
+                    for (int ks = 0; ks < D / 16; ++ks) {
+                        if (ks + AHEAD < D / 16)
+                            qa[ks + AHEAD] = lds_read16_early(qt + 32 * qh * RS + row_off + 16 * (ks + AHEAD));
+                        s = mfma_bf16_32x32x16(qa[ks], kf[ks], s);
+                    }
                 }
                 // Register i holds query 32 qh + c_row(i, h); four consecutive queries per float4.
                 float v[16];

@@ -76,6 +76,13 @@ __device__ __forceinline__ bf16x8 lds_read_tr_a(const bf16* p, int row_stride) {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// An LDS read that stays where it is written: a volatile access is neither
+// sunk towards its use nor merged with others, so the data is in flight while
+// the code in between runs.
+__device__ __forceinline__ bf16x8 lds_read16_early(const bf16* p) {
+    return *(const volatile __attribute__((address_space(3))) bf16x8*)(p);
+}
+
 // Workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2).
 // xcd_task() turns the flat id into a task index such that every XCD receives
 // a contiguous range of tasks; launch grid_for_tasks(total) workgroups and let

@@ -60,13 +60,6 @@ __device__ __forceinline__ bool wg_coords(int id, int BH, int nqb, bool causal, 
 // and most key tiles skip the alpha rescale of the accumulator.
 constexpr float kRescaleThreshold = 8.0f;
 
-// Reads of LDS that must stay where they are written: a volatile access is
-// neither sunk towards its use nor merged, so the data is in flight while the
-// code in between runs.
-__device__ __forceinline__ bf16x8 lds_read16_early(const bf16* p) {
-    return *(const volatile __attribute__((address_space(3))) bf16x8*)(p);
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
