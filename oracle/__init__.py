@@ -12,6 +12,9 @@ Functions take and return numpy float64 arrays laid out ``[BH, N, d]``
   scores), as on the "FlashAttention" deep-dive page, section "How it works".
 * :func:`attn_bwd` -- its analytic gradients (same page and section: D =
   rowsum(dO * O), dS = P * (dP - D), then dQ, dK, dV).
+* :func:`attn_fwd_gqa`, :func:`attn_bwd_gqa` -- the same with grouped heads
+  (GQA/MQA: several query heads share one key/value head; same page,
+  "Implementation notes"), gradients of shared K, V summed over the group.
 * :func:`attn_fwd_tiled` -- the per-query-block online-softmax loop of that
   page with deferred normalisation, used only to show tiled == untiled; it can
   trace the running (m, l, acc) of one row, which the worked example on the
@@ -63,6 +66,12 @@ def _load():
         lib.oracle_attn_fwd_rows.argtypes = [_f64p] * 3 + [ctypes.POINTER(_i64), _i64, _f64p, _f64p,
                                                            _i64, _i64, _i64, ctypes.c_double,
                                                            ctypes.c_int, ctypes.c_int]
+        lib.oracle_attn_fwd_gqa.argtypes = [_f64p] * 5 + [_i64] * 5 + [ctypes.c_double, ctypes.c_int,
+                                                                     ctypes.c_int]
+        lib.oracle_attn_bwd_gqa.argtypes = [_f64p] * 8 + [_i64] * 5 + [ctypes.c_double, ctypes.c_int,
+                                                                     ctypes.c_int]
+        lib.oracle_attn_fwd_gqa.restype = ctypes.c_int
+        lib.oracle_attn_bwd_gqa.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
         for fn in (lib.oracle_attn_fwd, lib.oracle_attn_bwd, lib.oracle_attn_fwd_tiled,
                    lib.oracle_attn_fwd_rows, lib.oracle_default_threads):
@@ -131,6 +140,47 @@ def attn_bwd(q, k, v, dout, scale, causal=False, threads=0):
     _check(_load().oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
                                    _ptr(dv), _ptr(delta), BH, N, d, float(scale),
                                    int(bool(causal)), _threads(threads)), "oracle_attn_bwd")
+    return dq, dk, dv, delta
+
+
+def _as4(x, name):
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    if a.ndim != 4:
+        raise ValueError(f"{name} must be [B, H, N, d]")
+    return a
+
+
+def attn_fwd_gqa(q, k, v, scale, causal=False, threads=0):
+    """Grouped-head forward: q [B, Hq, N, d], k, v [B, Hkv, N, d] with Hq a
+    multiple of Hkv; query head h uses key/value head h // (Hq // Hkv).
+    Returns (O [B, Hq, N, d], L [B, Hq, N]) in fp64."""
+    q, k, v = _as4(q, "q"), _as4(k, "k"), _as4(v, "v")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2:] != (N, d) or Hq % Hkv:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing Hq")
+    o = np.empty_like(q)
+    lse = np.empty((B, Hq, N), dtype=np.float64)
+    _check(_load().oracle_attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                                       float(scale), int(bool(causal)), _threads(threads)),
+           "oracle_attn_fwd_gqa")
+    return o, lse
+
+
+def attn_bwd_gqa(q, k, v, dout, scale, causal=False, threads=0):
+    """Grouped-head backward.  Returns (dQ [B, Hq, N, d], dK, dV [B, Hkv, N, d],
+    D [B, Hq, N]); dK, dV sum over the query heads sharing each key/value head."""
+    q, k, v, dout = _as4(q, "q"), _as4(k, "k"), _as4(v, "v"), _as4(dout, "dout")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if dout.shape != q.shape or k.shape != v.shape or k.shape[0] != B or k.shape[2:] != (N, d) or Hq % Hkv:
+        raise ValueError("bad shapes for the grouped-head backward")
+    dq = np.empty_like(q)
+    dk, dv = np.empty_like(k), np.empty_like(k)
+    delta = np.empty((B, Hq, N), dtype=np.float64)
+    _check(_load().oracle_attn_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                       _ptr(delta), B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
+                                       _threads(threads)), "oracle_attn_bwd_gqa")
     return dq, dk, dv, delta
 
 

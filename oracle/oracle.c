@@ -35,6 +35,13 @@
  * causal masks) gets O = 0 and L = -inf, as the deep-dive page's pitfalls
  * section prescribes for fully masked rows.
  *
+ * Grouped heads (GQA/MQA, "FlashAttention" deep-dive page, "Implementation
+ * notes"): the _gqa entry points take Hq query heads and Hkv = Hq / G key/value
+ * heads per batch; query head h of batch b attends with key/value head
+ * h / G of batch b.  The forward is the plain definition above with that
+ * head's K and V; K and V are shared by G query heads, so their gradients are
+ * the sums over those heads of the per-head dK and dV.
+ *
  * Parallelism: rows (forward, dQ) or keys (dK, dV) are split over POSIX
  * threads; every output element is computed by exactly one thread in a fixed
  * order, so results do not depend on the thread count.
@@ -114,16 +121,23 @@ typedef struct {
     int64_t N, d;
     double scale;
     int causal;
+    int64_t hq, group; /* query heads per batch, query heads per key/value head */
 } fwd_ctx;
+
+/* Key/value head (flat over batches) read by flat query head bh. */
+static int64_t kv_head(int64_t bh, int64_t hq, int64_t group) {
+    return (bh / hq) * (hq / group) + (bh % hq) / group;
+}
 
 /* One query row r = bh * N + i: scores of the visible keys, their maximum,
  * the softmax denominator, O_i = sum_j softmax_ij v_j and L_i = m + ln l. */
 static void fwd_one_row(const fwd_ctx* c, int64_t r, double* s, double* oi, double* lse_out) {
     const int64_t N = c->N, d = c->d;
     const int64_t bh = r / N, i = r % N;
+    const int64_t kvh = kv_head(bh, c->hq, c->group);
     const double* qi = c->q + r * d;
-    const double* kh = c->k + bh * N * d;
-    const double* vh = c->v + bh * N * d;
+    const double* kh = c->k + kvh * N * d;
+    const double* vh = c->v + kvh * N * d;
     double m = -INFINITY;
     for (int64_t j = 0; j < N; ++j) {
         if (!visible(c->causal, i, j)) continue;
@@ -177,15 +191,27 @@ int oracle_attn_fwd_rows(const double* q, const double* k, const double* v, cons
         return ORACLE_ERR_ARG;
     for (int64_t r = 0; r < nrows; ++r)
         if (rows[r] < 0 || rows[r] >= BH * N) return ORACLE_ERR_ARG;
-    fwd_rows_ctx c = {{q, k, v, o, lse, N, d, scale, causal}, rows};
+    fwd_rows_ctx c = {{q, k, v, o, lse, N, d, scale, causal, BH, 1}, rows};
     return parallel_for(nrows, nthreads, fwd_listed_rows, &c);
 }
 
 int oracle_attn_fwd(const double* q, const double* k, const double* v, double* o, double* lse,
                     int64_t BH, int64_t N, int64_t d, double scale, int causal, int nthreads) {
     if (!q || !k || !v || !o || !lse || BH <= 0 || N <= 0 || d <= 0) return ORACLE_ERR_ARG;
-    fwd_ctx c = {q, k, v, o, lse, N, d, scale, causal};
+    fwd_ctx c = {q, k, v, o, lse, N, d, scale, causal, BH, 1};
     return parallel_for(BH * N, nthreads, fwd_rows, &c);
+}
+
+/* Grouped-head forward: q, o [B, Hq, N, d], lse [B, Hq, N], k, v [B, Hkv, N, d],
+ * Hq a multiple of Hkv. */
+int oracle_attn_fwd_gqa(const double* q, const double* k, const double* v, double* o, double* lse,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, double scale,
+                        int causal, int nthreads) {
+    if (!q || !k || !v || !o || !lse || B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0 ||
+        Hq % Hkv != 0)
+        return ORACLE_ERR_ARG;
+    fwd_ctx c = {q, k, v, o, lse, N, d, scale, causal, Hq, Hq / Hkv};
+    return parallel_for(B * Hq * N, nthreads, fwd_rows, &c);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -246,32 +272,56 @@ static void bwd_rows(void* p, int64_t begin, int64_t end) {
     }
 }
 
-/* columns j: dV_j = sum_i P_ij dO_i ; dK_j = scale sum_i dS_ij q_i */
+/* columns j: dV_j += sum_i P_ij dO_i ; dK_j += scale sum_i dS_ij q_i (added to
+ * what dv, dk hold: the key/value head may be shared by several query heads) */
 static void bwd_cols(void* p, int64_t begin, int64_t end) {
     bwd_ctx* c = (bwd_ctx*)p;
     const int64_t N = c->N, d = c->d;
     for (int64_t j = begin; j < end; ++j) {
         double* dvj = c->dv + j * d;
         double* dkj = c->dk + j * d;
-        for (int64_t t = 0; t < d; ++t) dvj[t] = dkj[t] = 0.0;
-        for (int64_t i = 0; i < N; ++i) {
-            const double Pij = c->P[i * N + j], dSij = c->dS[i * N + j];
-            for (int64_t t = 0; t < d; ++t) {
-                dvj[t] += Pij * c->dout[i * d + t];
-                dkj[t] += dSij * c->q[i * d + t];
+        for (int64_t t = 0; t < d; ++t) {
+            double sv = 0.0, sk = 0.0;
+            for (int64_t i = 0; i < N; ++i) {
+                sv += c->P[i * N + j] * c->dout[i * d + t];
+                sk += c->dS[i * N + j] * c->q[i * d + t];
             }
+            dvj[t] += sv;
+            dkj[t] += c->scale * sk;
         }
-        for (int64_t t = 0; t < d; ++t) dkj[t] *= c->scale;
     }
 }
 
 /* delta may be NULL; otherwise it receives D = rowsum(dO * O) with the
  * oracle's own fp64 O. */
+static int bwd_grouped(const double* q, const double* k, const double* v, const double* dout,
+                       double* dq, double* dk, double* dv, double* delta, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t N, int64_t d, double scale, int causal, int nthreads);
+
 int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
                     double* dq, double* dk, double* dv, double* delta,
                     int64_t BH, int64_t N, int64_t d, double scale, int causal, int nthreads) {
     if (!q || !k || !v || !dout || !dq || !dk || !dv || BH <= 0 || N <= 0 || d <= 0)
         return ORACLE_ERR_ARG;
+    return bwd_grouped(q, k, v, dout, dq, dk, dv, delta, 1, BH, BH, N, d, scale, causal, nthreads);
+}
+
+/* Grouped-head backward: q, dout, dq [B, Hq, N, d], delta [B, Hq, N],
+ * k, v, dk, dv [B, Hkv, N, d], Hq a multiple of Hkv.  dk, dv are the sums
+ * over the query heads sharing each key/value head. */
+int oracle_attn_bwd_gqa(const double* q, const double* k, const double* v, const double* dout,
+                        double* dq, double* dk, double* dv, double* delta, int64_t B, int64_t Hq,
+                        int64_t Hkv, int64_t N, int64_t d, double scale, int causal, int nthreads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 ||
+        d <= 0 || Hq % Hkv != 0)
+        return ORACLE_ERR_ARG;
+    return bwd_grouped(q, k, v, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, scale, causal, nthreads);
+}
+
+static int bwd_grouped(const double* q, const double* k, const double* v, const double* dout,
+                       double* dq, double* dk, double* dv, double* delta, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t N, int64_t d, double scale, int causal, int nthreads) {
+    const int64_t BH = B * Hq, group = Hq / Hkv;
     double* P = (double*)malloc(sizeof(double) * (size_t)(N * N));
     double* dS = (double*)malloc(sizeof(double) * (size_t)(N * N));
     double* o = (double*)malloc(sizeof(double) * (size_t)(N * d));
@@ -279,9 +329,11 @@ int oracle_attn_bwd(const double* q, const double* k, const double* v, const dou
     double* dl = (double*)malloc(sizeof(double) * (size_t)N);
     int rc = ORACLE_OK;
     if (!P || !dS || !o || !lse || !dl) rc = ORACLE_ERR_NOMEM;
+    memset(dk, 0, sizeof(double) * (size_t)(B * Hkv * N * d));
+    memset(dv, 0, sizeof(double) * (size_t)(B * Hkv * N * d));
     for (int64_t bh = 0; bh < BH && rc == ORACLE_OK; ++bh) {
-        const int64_t off = bh * N * d;
-        bwd_ctx c = {q + off, k + off, v + off, dout + off, dq + off, dk + off, dv + off, dl,
+        const int64_t off = bh * N * d, kvoff = kv_head(bh, Hq, group) * N * d;
+        bwd_ctx c = {q + off, k + kvoff, v + kvoff, dout + off, dq + off, dk + kvoff, dv + kvoff, dl,
                      P, dS, o, lse, N, d, scale, causal};
         rc = parallel_for(N, nthreads, bwd_rows, &c);
         if (rc == ORACLE_OK) rc = parallel_for(N, nthreads, bwd_cols, &c);

@@ -334,3 +334,78 @@ def test_causal_backward_last_key_row0():
     S = 0.5 * q[0] @ k[0].T
     p_last = math.exp(S[N - 1, N - 1] - scipy.special.logsumexp(S[N - 1]))
     np.testing.assert_allclose(dv[0, N - 1], p_last * g[0, N - 1], atol=1e-14)
+
+
+# --- grouped heads (GQA / MQA) ------------------------------------------------
+
+def _gqa_inputs(seed, B, Hq, Hkv, N, d, with_dout=False):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, N, d))
+    k, v = (rng.standard_normal((B, Hkv, N, d)) for _ in range(2))
+    g = rng.standard_normal((B, Hq, N, d)) if with_dout else None
+    return q, k, v, g
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (6, 1), (3, 3)])
+def test_gqa_forward_against_torch_sdpa(Hq, Hkv):
+    """Grouped heads reduce to torch's fp64 scaled_dot_product_attention with
+    enable_gqa (query head h uses key/value head h // (Hq // Hkv)); L against
+    scipy's logsumexp of each head's scaled scores."""
+    torch = pytest.importorskip("torch")
+    B, N, d = 2, 23, 8
+    q, k, v, _ = _gqa_inputs(31, B, Hq, Hkv, N, d)
+    for causal in (False, True):
+        O, L = oracle.attn_fwd_gqa(q, k, v, 0.35, causal)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+            is_causal=causal, scale=0.35, enable_gqa=True).numpy()
+        np.testing.assert_allclose(O, ref, rtol=1e-12, atol=1e-12)
+        mask = np.tril(np.ones((N, N), dtype=bool)) if causal else np.ones((N, N), dtype=bool)
+        for b in range(B):
+            for h in range(Hq):
+                S = np.where(mask, 0.35 * q[b, h] @ k[b, h // (Hq // Hkv)].T, -np.inf)
+                np.testing.assert_allclose(L[b, h], scipy.special.logsumexp(S, axis=-1), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (5, 1)])
+def test_gqa_backward_against_torch_autograd_fp64(Hq, Hkv):
+    """Gradients of shared K and V are the sums over the query heads that use
+    them: torch's fp64 autograd through scaled_dot_product_attention."""
+    torch = pytest.importorskip("torch")
+    B, N, d = 2, 13, 8
+    q, k, v, g = _gqa_inputs(32, B, Hq, Hkv, N, d, with_dout=True)
+    for causal in (False, True):
+        dq, dk, dv, _ = oracle.attn_bwd_gqa(q, k, v, g, 0.5, causal)
+        tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+        O = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.5,
+                                                             enable_gqa=True)
+        O.backward(torch.tensor(g))
+        for got, t in zip((dq, dk, dv), (tq, tk, tv)):
+            np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_gqa_group_of_one_is_plain_attention():
+    """Hkv = Hq: the grouped entry points give the per-head oracle's results."""
+    B, H, N, d = 2, 3, 11, 4
+    q, k, v, g = _gqa_inputs(33, B, H, H, N, d, with_dout=True)
+    O, L = oracle.attn_fwd_gqa(q, k, v, 0.6, True)
+    O1, L1 = oracle.attn_fwd(q.reshape(B * H, N, d), k.reshape(B * H, N, d), v.reshape(B * H, N, d), 0.6, True)
+    np.testing.assert_array_equal(O.reshape(B * H, N, d), O1)
+    np.testing.assert_array_equal(L.reshape(B * H, N), L1)
+    grads = oracle.attn_bwd_gqa(q, k, v, g, 0.6, True)
+    grads1 = oracle.attn_bwd(*(x.reshape(B * H, N, d) for x in (q, k, v, g)), 0.6, True)
+    for a, b_ in zip(grads, grads1):
+        np.testing.assert_array_equal(a.reshape(b_.shape), b_)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_backward_invariants(causal):
+    """Per key/value head: sum_j dK_j = 0, and sum_j dV_j equals the sum of dO
+    over every row of the query heads in its group."""
+    B, Hq, Hkv, N, d = 2, 6, 2, 40, 8
+    q, k, v, g = _gqa_inputs(34, B, Hq, Hkv, N, d, with_dout=True)
+    dq, dk, dv, _ = oracle.attn_bwd_gqa(q, k, v, g, 0.3, causal)
+    G = Hq // Hkv
+    np.testing.assert_allclose(dk.sum(2), 0.0, atol=1e-12)
+    want = g.reshape(B, Hkv, G, N, d).sum(axis=(2, 3))
+    np.testing.assert_allclose(dv.sum(2), want, atol=1e-11)
