@@ -225,6 +225,7 @@ typedef struct {
     int64_t N, d;
     double scale;
     int causal;
+    int failed; /* set by a worker that could not allocate */
 } bwd_ctx;
 
 /* rows i: P_i, O_i, L_i, D_i, dS_i and dQ_i */
@@ -277,19 +278,30 @@ static void bwd_rows(void* p, int64_t begin, int64_t end) {
 static void bwd_cols(void* p, int64_t begin, int64_t end) {
     bwd_ctx* c = (bwd_ctx*)p;
     const int64_t N = c->N, d = c->d;
+    double* sv = (double*)malloc(sizeof(double) * (size_t)(2 * d));
+    if (!sv) {
+        c->failed = 1;
+        return;
+    }
+    double* sk = sv + d;
     for (int64_t j = begin; j < end; ++j) {
         double* dvj = c->dv + j * d;
         double* dkj = c->dk + j * d;
-        for (int64_t t = 0; t < d; ++t) {
-            double sv = 0.0, sk = 0.0;
-            for (int64_t i = 0; i < N; ++i) {
-                sv += c->P[i * N + j] * c->dout[i * d + t];
-                sk += c->dS[i * N + j] * c->q[i * d + t];
+        for (int64_t t = 0; t < d; ++t) sv[t] = sk[t] = 0.0;
+        /* each sum runs over i in increasing order */
+        for (int64_t i = 0; i < N; ++i) {
+            const double pij = c->P[i * N + j], dsij = c->dS[i * N + j];
+            for (int64_t t = 0; t < d; ++t) {
+                sv[t] += pij * c->dout[i * d + t];
+                sk[t] += dsij * c->q[i * d + t];
             }
-            dvj[t] += sv;
-            dkj[t] += c->scale * sk;
+        }
+        for (int64_t t = 0; t < d; ++t) {
+            dvj[t] += sv[t];
+            dkj[t] += c->scale * sk[t];
         }
     }
+    free(sv);
 }
 
 /* delta may be NULL; otherwise it receives D = rowsum(dO * O) with the
@@ -334,9 +346,10 @@ static int bwd_grouped(const double* q, const double* k, const double* v, const 
     for (int64_t bh = 0; bh < BH && rc == ORACLE_OK; ++bh) {
         const int64_t off = bh * N * d, kvoff = kv_head(bh, Hq, group) * N * d;
         bwd_ctx c = {q + off, k + kvoff, v + kvoff, dout + off, dq + off, dk + kvoff, dv + kvoff, dl,
-                     P, dS, o, lse, N, d, scale, causal};
+                     P, dS, o, lse, N, d, scale, causal, 0};
         rc = parallel_for(N, nthreads, bwd_rows, &c);
         if (rc == ORACLE_OK) rc = parallel_for(N, nthreads, bwd_cols, &c);
+        if (rc == ORACLE_OK && c.failed) rc = ORACLE_ERR_NOMEM;
         if (delta) memcpy(delta + bh * N, dl, sizeof(double) * (size_t)N);
     }
     free(P);
