@@ -52,7 +52,7 @@ extern "C" {
 
 typedef enum {
     FA_OK = 0,
-    FA_ERR_INVALID_ARG = 1, /* null pointer, B/H/N < 1, non-finite scale, size overflow */
+    FA_ERR_INVALID_ARG = 1, /* null pointer, B/H/N < 1, Hkv not dividing Hq, non-finite scale, size overflow */
     FA_ERR_UNSUPPORTED = 2, /* head dimension d not in {64, 128} */
     FA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
 } fa_status;
@@ -93,6 +93,29 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dO, float* dq, float* dk, float* dv, float* delta,
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Grouped heads (GQA; MQA when Hkv = 1): several query heads share one key
+ * and value head ("FlashAttention" deep-dive page, "Implementation notes":
+ * the query head maps to its key/value head).  Per batch there are Hq query
+ * heads and Hkv key/value heads, Hkv >= 1 dividing Hq; query head h of batch b
+ * attends with key/value head h / (Hq / Hkv) of batch b.
+ *
+ * fa_fwd_gqa: as fa_fwd with
+ *   q, o    : bf16 [B,Hq,N,d],   lse : float [B,Hq,N]
+ *   k, v    : bf16 [B,Hkv,N,d]
+ * fa_bwd_gqa: as fa_bwd with q, o, dO, dq [B,Hq,N,d], lse, delta [B,Hq,N] and
+ *   k, v, dk, dv [B,Hkv,N,d]; dk and dv are the sums of the gradients of the
+ *   Hq / Hkv query heads that share each key/value head (written, not
+ *   accumulated into; still bitwise reproducible).
+ * fa_fwd and fa_bwd are these with Hkv = Hq.  Errors as for fa_fwd/fa_bwd, plus
+ * FA_ERR_INVALID_ARG when Hkv < 1 or Hq % Hkv != 0.
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int N, int d, float scale, int causal, hipStream_t stream);
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dO, float* dq, float* dk, float* dv, float* delta,
+               int B, int Hq, int Hkv, int N, int d, float scale, int causal, hipStream_t stream);
 
 /*
  * The four stages of fa_bwd, for callers that schedule or time them

@@ -21,8 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_bwd_preprocess", "fa_bwd_dv", "fa_bwd_dk",
-           "fa_bwd_dq", "fa_status_string")
+SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_fwd_gqa", "fa_bwd_gqa", "fa_bwd_preprocess", "fa_bwd_dv",
+           "fa_bwd_dk", "fa_bwd_dq", "fa_status_string")
 
 
 class FaError(RuntimeError):
@@ -48,12 +48,14 @@ def load_library():
     lib.fa_fwd.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_fwd_f32.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
+    lib.fa_fwd_gqa.argtypes = [vp] * 5 + [i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_gqa.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
     lib.fa_bwd_preprocess.argtypes = [vp] * 3 + [i, i, i, i, vp]
     lib.fa_bwd_dv.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dk.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dq.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
-    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_bwd, lib.fa_bwd_preprocess, lib.fa_bwd_dv,
-               lib.fa_bwd_dk, lib.fa_bwd_dq):
+    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_bwd, lib.fa_fwd_gqa, lib.fa_bwd_gqa, lib.fa_bwd_preprocess,
+               lib.fa_bwd_dv, lib.fa_bwd_dk, lib.fa_bwd_dq):
         fn.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -153,6 +155,59 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, causal=False, scale=None, s
         raise FaError(st, "fa_bwd")
 
 
+def _gqa_shapes(q, k):
+    B, Hq, N, d = _shape(q)
+    Hkv = int(k.shape[1]) if k.dim() == 4 else -1
+    if k.dim() != 4 or tuple(k.shape) != (B, Hkv, N, d) or Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"k must be [B, Hkv, N, d] with Hkv dividing Hq={Hq}")
+    return B, Hq, Hkv, N, d
+
+
+def fa_fwd_gqa(q, k, v, o, lse, causal=False, scale=None, stream=None) -> None:
+    """Grouped-head bf16 forward: q, o [B,Hq,N,d], k, v [B,Hkv,N,d], lse fp32
+    [B,Hq,N]; query head h uses key/value head h // (Hq // Hkv)."""
+    B, Hq, Hkv, N, d = _gqa_shapes(q, k)
+    for t, n, shp in ((q, "q", (B, Hq, N, d)), (o, "o", (B, Hq, N, d)), (k, "k", (B, Hkv, N, d)),
+                      (v, "v", (B, Hkv, N, d))):
+        _check4(t, n, torch.bfloat16)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must have shape {shp}")
+    _check4(lse, "lse", torch.float32)
+    if tuple(lse.shape) != (B, Hq, N):
+        raise ValueError(f"lse must have shape {(B, Hq, N)}")
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, sc,
+                                   int(bool(causal)), ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_gqa")
+
+
+def fa_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, delta, causal=False, scale=None, stream=None) -> None:
+    """Grouped-head bf16 backward into caller-allocated fp32 dq [B,Hq,N,d],
+    dk, dv [B,Hkv,N,d] (sums over each group's query heads) and the fp32
+    workspace delta [B,Hq,N]."""
+    B, Hq, Hkv, N, d = _gqa_shapes(q, k)
+    for t, n, shp in ((q, "q", (B, Hq, N, d)), (o, "o", (B, Hq, N, d)), (dout, "dout", (B, Hq, N, d)),
+                      (k, "k", (B, Hkv, N, d)), (v, "v", (B, Hkv, N, d))):
+        _check4(t, n, torch.bfloat16)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must have shape {shp}")
+    for t, n, shp in ((dq, "dq", (B, Hq, N, d)), (dk, "dk", (B, Hkv, N, d)), (dv, "dv", (B, Hkv, N, d))):
+        _check4(t, n, torch.float32)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must have shape {shp}")
+    for t, n in ((lse, "lse"), (delta, "delta")):
+        _check4(t, n, torch.float32)
+        if tuple(t.shape) != (B, Hq, N):
+            raise ValueError(f"{n} must have shape {(B, Hq, N)}")
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), _ptr(delta), B, Hq, Hkv, N, d, sc, int(bool(causal)),
+                                   ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_gqa")
+
+
 def _check_bwd_args(q, k, v, dout, lse, delta, outs):
     B, H, N, d = _shape(q)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
@@ -229,23 +284,29 @@ def fa_bwd_dq(q, k, v, lse, dout, delta, dq, causal=False, scale=None, stream=No
 
 
 def attention_fwd(q, k, v, causal=False, scale=None, stream=None):
-    """Allocating wrapper: returns (o, lse).  bf16 or fp32 inputs."""
+    """Allocating wrapper: returns (o, lse).  bf16 or fp32 inputs; bf16 k, v
+    with fewer heads than q select the grouped-head entry point."""
     B, H, N, d = _shape(q)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     if q.dtype == torch.float32:
         fa_fwd_f32(q, k, v, o, lse, causal, scale, stream)
+    elif k.dim() == 4 and k.shape[1] != H:
+        fa_fwd_gqa(q, k, v, o, lse, causal, scale, stream)
     else:
         fa_fwd(q, k, v, o, lse, causal, scale, stream)
     return o, lse
 
 
 def attention_bwd(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):
-    """Allocating wrapper: returns (dq, dk, dv) in fp32."""
+    """Allocating wrapper: returns (dq, dk, dv) in fp32 (dk, dv shaped like k)."""
     B, H, N, d = _shape(q)
     dq = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
-    dk = torch.empty_like(dq)
-    dv = torch.empty_like(dq)
+    dk = torch.empty(tuple(k.shape), dtype=torch.float32, device=q.device)
+    dv = torch.empty_like(dk)
     delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, causal, scale, stream)
+    if k.dim() == 4 and k.shape[1] != H:
+        fa_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, delta, causal, scale, stream)
+    else:
+        fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, causal, scale, stream)
     return dq, dk, dv

@@ -115,11 +115,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_preprocess_kernel(const bf16*
 constexpr int kDkvBq = 64;    // query rows per step
 constexpr int kDkvBkv = 32 * kBwdWaves;  // keys per workgroup
 
-template <int D, bool CAUSAL, bool DK>
+// GROUPED: several query heads per key/value head (G = Hq / Hkv > 1).  Without
+// it G is the constant 1 and the group loop disappears at compile time.
+template <int D, bool CAUSAL, bool DK, bool GROUPED>
 __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    float* __restrict__ dOut, int N, int BH, int nkb, float scale_log2, float out_scale) {
+    float* __restrict__ dOut, int N, int BKV, int nkb, float scale_log2, float out_scale, int Hq, int G_arg) {
+    const int G = GROUPED ? G_arg : 1;
     constexpr int BQ = kDkvBq;
     constexpr int RS = both_ways_stride<D>();
     __shared__ __attribute__((aligned(16))) bf16 sQ[2][BQ * RS];
@@ -129,20 +132,21 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int lq = lane & 31, h = lane >> 5;
-    // Flat id -> (head, key block): XCD-contiguous, head-major; key blocks
-    // ascend, so for causal masks the heaviest blocks (the first ones, seen by
-    // the most queries) start first.
-    const int task = xcd_task(blockIdx.x, BH * nkb);
-    if (task >= BH * nkb) return;
-    const int bh = task / nkb;
+    // Flat id -> (key/value head, key block): XCD-contiguous, head-major; key
+    // blocks ascend, so for causal masks the heaviest blocks (the first ones,
+    // seen by the most queries) start first.  The G query heads sharing the
+    // key/value head (grouped heads) are walked one after the other, their
+    // contributions summed in the same accumulators.
+    const int task = xcd_task(blockIdx.x, BKV * nkb);
+    if (task >= BKV * nkb) return;
+    const int kvh = task / nkb;
     const int kb = task % nkb;
     const int k0 = kb * kDkvBkv;
     const int kw0 = k0 + 32 * w;
     const int key = kw0 + lq;
-    const int64_t base = (int64_t)bh * N * D;
+    const int64_t base = (int64_t)kvh * N * D;
+    const int qh0 = (kvh / (Hq / G)) * Hq + (kvh % (Hq / G)) * G;  // first query head of the group
     const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
-    const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + base, head_bytes);
 
     // K^T (and, for dK, V^T) operands of this lane's key (zero past N).
     bf16x8 kf[D / 16], vf[DK ? D / 16 : 1];
@@ -162,115 +166,127 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
 
     const int nqblk = (N + BQ - 1) / BQ;
     const int iq0 = CAUSAL ? k0 / BQ : 0;
+    // Steps whose query block starts before this workgroup's last key.
+    const int iq_split = CAUSAL ? min(nqblk, (k0 + kDkvBkv - 1) / BQ + 1) : iq0;
     TileStager<D, BQ> stq(tid, RS), stg(tid, RS);
     float lreg = 0.f, dreg = 0.f;
-    const float* lse_h = LSE + (int64_t)bh * N;
-    const float* d_h = Dl + (int64_t)bh * N;
-    auto load_block = [&](int iq) {
-        const int i0 = iq * BQ;
-        stq.load(qrs, i0);
-        stg.load(grs, i0);
-        if (tid < BQ) {
-            const int r = min(i0 + tid, N - 1);
-            lreg = i0 + tid < N ? lse_h[r] * kLog2e : INFINITY;  // P = 0 past N
-            if constexpr (DK) dreg = i0 + tid < N ? d_h[r] : 0.f;
-        }
-    };
-    auto store_block = [&](int buf) {
-        stq.store(sQ[buf], RS);
-        stg.store(sdO[buf], RS);
-        if (tid < BQ) {
-            sL[buf][tid] = lreg;
-            if constexpr (DK) sD[buf][tid] = dreg;
-        }
-    };
     // Per-lane LDS offsets: 16-byte rows and transposing reads.
     const int row_off = lq * RS + 8 * h;
     const int tr_off = tr_row(lane) * RS + tr_col(lane);
 
-    // Loads and stores are unconditional (the last step re-stages the final
-    // block into the idle buffer) so that no math waits on a pending load.
-    if (iq0 < nqblk) {
-        load_block(iq0);
-        store_block(0);
-    }
-    __syncthreads();
-    // One step of 64 query rows.  MASK applies the causal mask; only the steps
-    // whose queries overlap this workgroup's keys (the first two) need it, so
-    // the loop is split and the other steps carry no mask code.
-    auto step = [&](int iq, auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        const int buf = (iq - iq0) & 1;
-        load_block(min(iq + 1, nqblk - 1));
-        const int i0 = iq * BQ;
-        // Skip blocks whose every query precedes every key of this wave.
-        if (!CAUSAL || __builtin_amdgcn_readfirstlane(i0 + BQ - 1 >= kw0)) {
-            const bf16* qt = sQ[buf];
-            const bf16* gt = sdO[buf];
-#pragma unroll
-            for (int qh = 0; qh < BQ / 32; ++qh) {
-                f32x16 s = f32x16{}, dp = f32x16{};
-                if constexpr (DK) {
-#pragma unroll
-                    for (int ks = 0; ks < D / 16; ++ks) {
-                        s = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(qt + 32 * qh * RS + row_off + 16 * ks),
-                                               kf[ks], s);
-                        dp = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(gt + 32 * qh * RS + row_off + 16 * ks),
-                                                vf[ks], dp);
-                    }
-                } else {
-                    // dV has registers to spare: each Q fragment is requested four
-                    // MFMAs before its use (volatile reads keep that order).
-                    constexpr int AHEAD = 4;
-                    bf16x8 qa[D / 16];
-#pragma unroll
-                    for (int ks = 0; ks < AHEAD; ++ks)
-                        qa[ks] = lds_read16_early(qt + 32 * qh * RS + row_off + 16 * ks);
-#pragma unroll
-                    for (int ks = 0; ks < D / 16; ++ks) {
-                        if (ks + AHEAD < D / 16)
-                            qa[ks + AHEAD] = lds_read16_early(qt + 32 * qh * RS + row_off + 16 * (ks + AHEAD));
-                        s = mfma_bf16_32x32x16(qa[ks], kf[ks], s);
-                    }
-                }
-                // Register i holds query 32 qh + c_row(i, h); four consecutive queries per float4.
-                float v[16];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][32 * qh + 8 * r + 4 * h]);
-                    f32x4 d4 = f32x4{};
-                    if constexpr (DK) d4 = *reinterpret_cast<const f32x4*>(&sD[buf][32 * qh + 8 * r + 4 * h]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 4 * r + e;
-                        float p = fast_exp2(fmaf(s[i], scale_log2, -l4[e]));
-                        if constexpr (MASK) {
-                            if (key > i0 + 32 * qh + c_row(i, h)) p = 0.f;
-                        }
-                        v[i] = DK ? p * (dp[i] - d4[e]) : p;
-                    }
-                }
-                // B operand (P for dV, dS for dK) of k-steps 0 and 1.
-                const bf16x8 bop0 = pack_bf16x8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
-                const bf16x8 bop1 = pack_bf16x8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
-                // k-step s2 covers queries 32 qh + 16 s2 + {4h + e, 8 + 4h + e}.
-                const bf16* at = DK ? qt : gt;  // A = Q^T (dK) or dO^T (dV)
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-                    acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(at + 32 * qh * RS + tr_off + 32 * db, RS), bop0, acc[db]);
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-                    acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(at + (32 * qh + 16) * RS + tr_off + 32 * db, RS), bop1,
-                                                 acc[db]);
+    // All query blocks of query head qh (one of the group sharing this
+    // key/value head), accumulated into acc.  The head's bases are set up
+    // once, outside its step loop.
+    auto run_head = [&](int qh_idx) {
+        const int64_t qbase = (int64_t)qh_idx * N;
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + qbase * D, head_bytes);
+        const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + qbase * D, head_bytes);
+        const float* lse_h = LSE + qbase;
+        const float* d_h = Dl + qbase;
+        auto load_block = [&](int iq) {
+            const int i0 = iq * BQ;
+            stq.load(qrs, i0);
+            stg.load(grs, i0);
+            if (tid < BQ) {
+                const int r = min(i0 + tid, N - 1);
+                lreg = i0 + tid < N ? lse_h[r] * kLog2e : INFINITY;  // P = 0 past N
+                if constexpr (DK) dreg = i0 + tid < N ? d_h[r] : 0.f;
             }
+        };
+        auto store_block = [&](int buf) {
+            stq.store(sQ[buf], RS);
+            stg.store(sdO[buf], RS);
+            if (tid < BQ) {
+                sL[buf][tid] = lreg;
+                if constexpr (DK) sD[buf][tid] = dreg;
+            }
+        };
+
+        // Loads and stores are unconditional (the last step re-stages the final
+        // block into the idle buffer) so that no math waits on a pending load.
+        if (iq0 < nqblk) {
+            load_block(iq0);
+            store_block(0);
         }
-        store_block(buf ^ 1);
         __syncthreads();
+        // One step of 64 query rows.  MASK applies the causal mask; only the
+        // steps whose queries overlap this workgroup's keys (the first two)
+        // need it, so the loop is split and the other steps carry no mask code.
+        auto step = [&](int iq, auto mask_tag) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            const int buf = (iq - iq0) & 1;
+            load_block(min(iq + 1, nqblk - 1));
+            const int i0 = iq * BQ;
+            // Skip blocks whose every query precedes every key of this wave.
+            if (!CAUSAL || __builtin_amdgcn_readfirstlane(i0 + BQ - 1 >= kw0)) {
+                const bf16* qt = sQ[buf];
+                const bf16* gt = sdO[buf];
+#pragma unroll
+                for (int qh = 0; qh < BQ / 32; ++qh) {
+                    f32x16 s = f32x16{}, dp = f32x16{};
+                    if constexpr (DK) {
+#pragma unroll
+                        for (int ks = 0; ks < D / 16; ++ks) {
+                            const int off = 32 * qh * RS + row_off + 16 * ks;
+                            s = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(qt + off), kf[ks], s);
+                            dp = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(gt + off), vf[ks], dp);
+                        }
+                    } else {
+                        // dV has registers to spare: each Q fragment is requested four
+                        // MFMAs before its use (volatile reads keep that order).
+                        constexpr int AHEAD = 4;
+                        bf16x8 qa[D / 16];
+#pragma unroll
+                        for (int ks = 0; ks < AHEAD; ++ks)
+                            qa[ks] = lds_read16_early(qt + 32 * qh * RS + row_off + 16 * ks);
+#pragma unroll
+                        for (int ks = 0; ks < D / 16; ++ks) {
+                            if (ks + AHEAD < D / 16)
+                                qa[ks + AHEAD] = lds_read16_early(qt + 32 * qh * RS + row_off + 16 * (ks + AHEAD));
+                            s = mfma_bf16_32x32x16(qa[ks], kf[ks], s);
+                        }
+                    }
+                    // Register i holds query 32 qh + c_row(i, h); four consecutive queries per float4.
+                    float v[16];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][32 * qh + 8 * r + 4 * h]);
+                        f32x4 d4 = f32x4{};
+                        if constexpr (DK) d4 = *reinterpret_cast<const f32x4*>(&sD[buf][32 * qh + 8 * r + 4 * h]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int i = 4 * r + e;
+                            float p = fast_exp2(fmaf(s[i], scale_log2, -l4[e]));
+                            if constexpr (MASK) {
+                                if (key > i0 + 32 * qh + c_row(i, h)) p = 0.f;
+                            }
+                            v[i] = DK ? p * (dp[i] - d4[e]) : p;
+                        }
+                    }
+                    // B operand (P for dV, dS for dK) of k-steps 0 and 1.
+                    const bf16x8 bop0 = pack_bf16x8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+                    const bf16x8 bop1 = pack_bf16x8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
+                    // k-step s2 covers queries 32 qh + 16 s2 + {4h + e, 8 + 4h + e}.
+                    const bf16* at = DK ? qt : gt;  // A = Q^T (dK) or dO^T (dV)
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+                        acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(at + 32 * qh * RS + tr_off + 32 * db, RS), bop0,
+                                                     acc[db]);
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+                        acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(at + (32 * qh + 16) * RS + tr_off + 32 * db, RS),
+                                                     bop1, acc[db]);
+                }
+            }
+            store_block(buf ^ 1);
+            __syncthreads();
+        };
+        for (int iq = iq0; iq < iq_split; ++iq) step(iq, std::true_type{});
+        for (int iq = max(iq0, iq_split); iq < nqblk; ++iq) step(iq, std::false_type{});
     };
-    // Steps whose query block starts before this workgroup's last key.
-    const int iq_split = CAUSAL ? min(nqblk, (k0 + kDkvBkv - 1) / BQ + 1) : iq0;
-    for (int iq = iq0; iq < iq_split; ++iq) step(iq, std::true_type{});
-    for (int iq = max(iq0, iq_split); iq < nqblk; ++iq) step(iq, std::false_type{});
+    // Grouped heads: the G query heads sharing this key/value head one after
+    // the other, their contributions summed in the same accumulators.
+    for (int g = 0; g < G; ++g) run_head(qh0 + g);
 
     // Register i of block db holds dim 32 db + c_row(i, h) of this lane's key.
     if (key < N) {
@@ -301,7 +317,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    float* __restrict__ dQ, int N, int BH, int nqb, float scale_log2, float scale) {
+    float* __restrict__ dQ, int N, int BH, int nqb, float scale_log2, float scale, int Hq, int G) {
     constexpr int BKV = kDqBkv;
     constexpr int KS = both_ways_stride<D>();
     constexpr int VS = D + 8;  // rows only
@@ -319,9 +335,10 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
     const int qw0 = q0 + 32 * w;
     const int qrow = qw0 + lq;
     const int64_t base = (int64_t)bh * N * D;
+    const int64_t kv_base = (int64_t)kv_head(bh, Hq, G) * N * D;  // grouped heads share K, V
     const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_base, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_base, head_bytes);
 
     bf16x8 qf[D / 16], gf[D / 16];
     {
@@ -431,81 +448,84 @@ hipError_t launch_pre_t(const bf16* o, const bf16* dout, float* delta, int BH, i
 
 template <int D, bool CAUSAL, bool DK>
 hipError_t launch_dkdv_t(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
-                         const float* delta, float* out, int BH, int N, float scale, hipStream_t stream) {
-    const int nkb = (N + kDkvBkv - 1) / kDkvBkv;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK>), dim3(grid_for_tasks(nkb * BH)), dim3(kBwdThreads), 0, stream,
-                       q, k, v, dout, lse, delta, out, N, BH, nkb, scale * kLog2e, DK ? scale : 1.0f);
+                         const float* delta, float* out, int B, int Hq, int Hkv, int N, float scale,
+                         hipStream_t stream) {
+    const int nkb = (N + kDkvBkv - 1) / kDkvBkv, BKV = B * Hkv;
+    const dim3 grid(grid_for_tasks(nkb * BKV));
+    if (Hq == Hkv)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK, false>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout,
+                           lse, delta, out, N, BKV, nkb, scale * kLog2e, DK ? scale : 1.0f, Hq, 1);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK, true>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout,
+                           lse, delta, out, N, BKV, nkb, scale * kLog2e, DK ? scale : 1.0f, Hq, Hq / Hkv);
     return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
-                       const float* delta, float* dq, int BH, int N, float scale, hipStream_t stream) {
-    const int nqb = (N + kDqBq - 1) / kDqBq;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(grid_for_tasks(nqb * BH)), dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                       lse, delta, dq, N, BH, nqb, scale * kLog2e, scale);
+                       const float* delta, float* dq, int B, int Hq, int Hkv, int N, float scale, hipStream_t stream) {
+    const int nqb = (N + kDqBq - 1) / kDqBq, BH = B * Hq;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(grid_for_tasks(nqb * BH)), dim3(kBwdThreads), 0, stream, q, k,
+                       v, dout, lse, delta, dq, N, BH, nqb, scale * kLog2e, scale, Hq, Hq / Hkv);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int BH, int N, int d,
+hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int BHq, int N, int d,
                                  hipStream_t stream) {
     auto Op = static_cast<const bf16*>(o);
     auto G = static_cast<const bf16*>(dout);
-    return d == 64 ? launch_pre_t<64>(Op, G, delta, BH, N, stream) : launch_pre_t<128>(Op, G, delta, BH, N, stream);
+    return d == 64 ? launch_pre_t<64>(Op, G, delta, BHq, N, stream) : launch_pre_t<128>(Op, G, delta, BHq, N, stream);
 }
 
-hipError_t launch_bwd_dv(const void* q, const void* k, const float* lse, const void* dout, float* dv, int BH,
-                         int N, int d, float scale, bool causal, hipStream_t stream) {
+hipError_t launch_bwd_dv(const void* q, const void* k, const float* lse, const void* dout, float* dv, int B, int Hq,
+                         int Hkv, int N, int d, float scale, bool causal, hipStream_t stream) {
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
     auto G = static_cast<const bf16*>(dout);
-    if (d == 64)
-        return causal ? launch_dkdv_t<64, true, false>(Q, K, K, lse, G, nullptr, dv, BH, N, scale, stream)
-                      : launch_dkdv_t<64, false, false>(Q, K, K, lse, G, nullptr, dv, BH, N, scale, stream);
-    return causal ? launch_dkdv_t<128, true, false>(Q, K, K, lse, G, nullptr, dv, BH, N, scale, stream)
-                  : launch_dkdv_t<128, false, false>(Q, K, K, lse, G, nullptr, dv, BH, N, scale, stream);
+#define FA_DV(DD, CC) launch_dkdv_t<DD, CC, false>(Q, K, K, lse, G, nullptr, dv, B, Hq, Hkv, N, scale, stream)
+    if (d == 64) return causal ? FA_DV(64, true) : FA_DV(64, false);
+    return causal ? FA_DV(128, true) : FA_DV(128, false);
+#undef FA_DV
 }
 
 hipError_t launch_bwd_dk(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                         const float* delta, float* dk, int BH, int N, int d, float scale, bool causal,
+                         const float* delta, float* dk, int B, int Hq, int Hkv, int N, int d, float scale, bool causal,
                          hipStream_t stream) {
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
     auto V = static_cast<const bf16*>(v);
     auto G = static_cast<const bf16*>(dout);
-    if (d == 64)
-        return causal ? launch_dkdv_t<64, true, true>(Q, K, V, lse, G, delta, dk, BH, N, scale, stream)
-                      : launch_dkdv_t<64, false, true>(Q, K, V, lse, G, delta, dk, BH, N, scale, stream);
-    return causal ? launch_dkdv_t<128, true, true>(Q, K, V, lse, G, delta, dk, BH, N, scale, stream)
-                  : launch_dkdv_t<128, false, true>(Q, K, V, lse, G, delta, dk, BH, N, scale, stream);
+#define FA_DK(DD, CC) launch_dkdv_t<DD, CC, true>(Q, K, V, lse, G, delta, dk, B, Hq, Hkv, N, scale, stream)
+    if (d == 64) return causal ? FA_DK(64, true) : FA_DK(64, false);
+    return causal ? FA_DK(128, true) : FA_DK(128, false);
+#undef FA_DK
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                         const float* delta, float* dq, int BH, int N, int d, float scale, bool causal,
+                         const float* delta, float* dq, int B, int Hq, int Hkv, int N, int d, float scale, bool causal,
                          hipStream_t stream) {
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
     auto V = static_cast<const bf16*>(v);
     auto G = static_cast<const bf16*>(dout);
-    if (d == 64)
-        return causal ? launch_dq_t<64, true>(Q, K, V, lse, G, delta, dq, BH, N, scale, stream)
-                      : launch_dq_t<64, false>(Q, K, V, lse, G, delta, dq, BH, N, scale, stream);
-    return causal ? launch_dq_t<128, true>(Q, K, V, lse, G, delta, dq, BH, N, scale, stream)
-                  : launch_dq_t<128, false>(Q, K, V, lse, G, delta, dq, BH, N, scale, stream);
+#define FA_DQ(DD, CC) launch_dq_t<DD, CC>(Q, K, V, lse, G, delta, dq, B, Hq, Hkv, N, scale, stream)
+    if (d == 64) return causal ? FA_DQ(64, true) : FA_DQ(64, false);
+    return causal ? FA_DQ(128, true) : FA_DQ(128, false);
+#undef FA_DQ
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                           const void* dout, float* dq, float* dk, float* dv, float* delta, int BH, int N,
-                           int d, float scale, bool causal, hipStream_t stream) {
-    hipError_t e = launch_bwd_preprocess(o, dout, delta, BH, N, d, stream);
+                           const void* dout, float* dq, float* dk, float* dv, float* delta, int B, int Hq, int Hkv,
+                           int N, int d, float scale, bool causal, hipStream_t stream) {
+    hipError_t e = launch_bwd_preprocess(o, dout, delta, B * Hq, N, d, stream);
     if (e != hipSuccess) return e;
-    e = launch_bwd_dv(q, k, lse, dout, dv, BH, N, d, scale, causal, stream);
+    e = launch_bwd_dv(q, k, lse, dout, dv, B, Hq, Hkv, N, d, scale, causal, stream);
     if (e != hipSuccess) return e;
-    e = launch_bwd_dk(q, k, v, lse, dout, delta, dk, BH, N, d, scale, causal, stream);
+    e = launch_bwd_dk(q, k, v, lse, dout, delta, dk, B, Hq, Hkv, N, d, scale, causal, stream);
     if (e != hipSuccess) return e;
-    return launch_bwd_dq(q, k, v, lse, dout, delta, dq, BH, N, d, scale, causal, stream);
+    return launch_bwd_dq(q, k, v, lse, dout, delta, dq, B, Hq, Hkv, N, d, scale, causal, stream);
 }
 
 }  // namespace fa

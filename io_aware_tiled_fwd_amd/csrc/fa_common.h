@@ -97,6 +97,10 @@ __device__ __forceinline__ int xcd_task(int id, int total) {
     return (id % kNumXcd) * per + id / kNumXcd;
 }
 
+// Key/value head (flat over batches) read by flat query head bh, with Hq
+// query heads per batch and G query heads per key/value head.
+__device__ __forceinline__ int kv_head(int bh, int Hq, int G) { return (bh / Hq) * (Hq / G) + (bh % Hq) / G; }
+
 // Buffer resource over [base, base + bytes): raw buffer loads whose byte offset
 // (VGPR offset + SGPR offset) falls outside return zero (range checking of
 // untyped buffer loads; the SGPR offset takes part, checked on hardware).  A

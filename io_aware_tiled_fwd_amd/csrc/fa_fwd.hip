@@ -63,7 +63,7 @@ constexpr float kRescaleThreshold = 8.0f;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, float scale_log2) {
+    bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, float scale_log2, int Hq, int G) {
     constexpr int BC = kFwdBc;
     constexpr int KS = D + 8;   // K row stride: 16 consecutive rows hit distinct banks (b128 reads)
     constexpr int VTS = BC + 8;  // V^T row stride, same property
@@ -85,12 +85,13 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     const int qw0 = q0 + 32 * w;  // first query row of this wave
     const int qrow = qw0 + lq;    // this lane's query row
     const int64_t base = (int64_t)bh * N * D;
+    const int64_t kv_base = (int64_t)kv_head(bh, Hq, G) * N * D;  // grouped heads share K, V
 
     // Per-head buffer resources: rows past N read as zero.
     const uint32_t head_bytes = (uint32_t)N * D * 2;
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + base, head_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_base, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_base, head_bytes);
 
     // Q^T operand: k-step ks holds Q[qrow][16 ks + 8 h .. +7].
     bf16x8 qf[NKS];
@@ -398,8 +399,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_f32_kernel(
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                           int N, int d, float scale, bool causal, hipStream_t stream) {
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                           int Hkv, int N, int d, float scale, bool causal, hipStream_t stream) {
+    const int BH = B * Hq, G = Hq / Hkv;
     const int nqb = (N + kFwdBr - 1) / kFwdBr;
     const int grid = grid_for_tasks(nqb * BH);
     const float sl2 = scale * kLog2e;
@@ -410,7 +412,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 #define FA_FWD_LAUNCH(DD, CC)                                                                          \
     do {                                                                                               \
         hipLaunchKernelGGL((fwd_bf16_kernel<DD, CC>), dim3(grid), dim3(kFwdThreads), 0, stream, Q, K, V, \
-                           Op, lse, N, BH, nqb, sl2);                                                  \
+                           Op, lse, N, BH, nqb, sl2, Hq, G);                                           \
         return hipGetLastError();                                                                      \
     } while (0)
     if (d == 64) {

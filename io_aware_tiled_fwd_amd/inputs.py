@@ -69,6 +69,20 @@ def normal_qkv(B, H, N, d, seed, dtype="bf16", with_dout=False) -> Tensors:
     return Tensors(names, dtype, bits, f64)
 
 
+def normal_gqa(B, Hq, Hkv, N, d, seed, with_dout=False) -> Tensors:
+    """Grouped heads: Q (and dO) [B, Hq, N, d], K, V [B, Hkv, N, d], i.i.d.
+    N(0,1) from ``numpy.random.default_rng(seed)`` in the order Q, K, V, dO,
+    stored as bf16."""
+    rng = np.random.default_rng(seed)
+    names = ("q", "k", "v", "do") if with_dout else ("q", "k", "v")
+    bits, f64 = {}, {}
+    for n in names:
+        heads = Hkv if n in ("k", "v") else Hq
+        bits[n] = bf16_bits(rng.standard_normal((B, heads, N, d), dtype=np.float32))
+        f64[n] = bf16_to_f64(bits[n])
+    return Tensors(names, "bf16", bits, f64)
+
+
 def page_generator(n, d, seed) -> np.ndarray:
     """The deterministic fp32 generator of the deep-dive page's self-test:
     element i (row-major over n x d) is ((i * 7919 + seed) mod 1000) / 500 - 1."""

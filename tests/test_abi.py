@@ -109,6 +109,30 @@ def test_bwd_rejects_bad_arguments(lib):
     assert call(ptrs) == 1
 
 
+def test_gqa_rejects_bad_arguments(lib):
+    """Grouped heads: Hkv must be >= 1 and divide Hq; the shape checks of the
+    per-head entry points apply to Hq."""
+    def fwd(ptrs, B=1, Hq=4, Hkv=2, N=16, d=128, scale=0.1):
+        return lib.fa_fwd_gqa(*ptrs, B, Hq, Hkv, N, d, ctypes.c_float(scale), 1, NUL)
+
+    def bwd(ptrs, B=1, Hq=4, Hkv=2, N=16, d=128, scale=0.1):
+        return lib.fa_bwd_gqa(*ptrs, B, Hq, Hkv, N, d, ctypes.c_float(scale), 1, NUL)
+
+    for call, n in ((fwd, 5), (bwd, 10)):
+        ok = [FAKE] * n
+        for i in range(n):
+            ptrs = list(ok)
+            ptrs[i] = NUL
+            assert call(ptrs) == 1
+        assert call(ok, Hkv=0) == 1
+        assert call(ok, Hkv=-2) == 1
+        assert call(ok, Hq=6, Hkv=4) == 1
+        assert call(ok, Hq=2, Hkv=4) == 1
+        assert call(ok, Hq=0, Hkv=1) == 1
+        assert call(ok, d=96) == 2
+        assert call(ok, scale=float("nan")) == 1
+
+
 def test_package_import_does_not_load_library():
     import importlib
     import io_aware_tiled_fwd_amd.inputs  # noqa: F401
