@@ -15,6 +15,10 @@ Functions take and return numpy float64 arrays laid out ``[BH, N, d]``
 * :func:`attn_fwd_gqa`, :func:`attn_bwd_gqa` -- the same with grouped heads
   (GQA/MQA: several query heads share one key/value head; same page,
   "Implementation notes"), gradients of shared K, V summed over the group.
+* :func:`attn_decode` -- one query row per (batch, query head) against a
+  key/value cache of which the first ``kv_len[b]`` keys are visible (the
+  single-query decode of the deep-dive page, "Implementation notes"); the plain
+  definition again.
 * :func:`attn_fwd_tiled` -- the per-query-block online-softmax loop of that
   page with deferred normalisation, used only to show tiled == untiled; it can
   trace the running (m, l, acc) of one row, which the worked example on the
@@ -70,6 +74,9 @@ def _load():
                                                                      ctypes.c_int]
         lib.oracle_attn_bwd_gqa.argtypes = [_f64p] * 8 + [_i64] * 5 + [ctypes.c_double, ctypes.c_int,
                                                                      ctypes.c_int]
+        lib.oracle_attn_decode.argtypes = [_f64p] * 3 + [ctypes.POINTER(_i64), _f64p, _f64p] + [_i64] * 5 + [
+            ctypes.c_double, ctypes.c_int]
+        lib.oracle_attn_decode.restype = ctypes.c_int
         lib.oracle_attn_fwd_gqa.restype = ctypes.c_int
         lib.oracle_attn_bwd_gqa.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
@@ -182,6 +189,32 @@ def attn_bwd_gqa(q, k, v, dout, scale, causal=False, threads=0):
                                        _ptr(delta), B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
                                        _threads(threads)), "oracle_attn_bwd_gqa")
     return dq, dk, dv, delta
+
+
+def attn_decode(q, k, v, scale, kv_len=None, threads=0):
+    """Decode: q [B, Hq, d] (one query row per head), k, v [B, Hkv, Nk, d],
+    Hkv dividing Hq; batch b sees keys j < kv_len[b] (all Nk when kv_len is
+    None).  Returns (O [B, Hq, d], L [B, Hq]) in fp64."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k, v = _as4(k, "k"), _as4(v, "v")
+    if q.ndim != 3:
+        raise ValueError("q must be [B, Hq, d]")
+    B, Hq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d or Hq % Hkv:
+        raise ValueError("k, v must be [B, Hkv, Nk, d] with Hkv dividing Hq")
+    lens = None
+    if kv_len is not None:
+        lens = np.ascontiguousarray(kv_len, dtype=np.int64)
+        if lens.shape != (B,):
+            raise ValueError("kv_len must have one entry per batch")
+    o = np.empty_like(q)
+    lse = np.empty((B, Hq), dtype=np.float64)
+    _check(_load().oracle_attn_decode(_ptr(q), _ptr(k), _ptr(v),
+                                      lens.ctypes.data_as(ctypes.POINTER(_i64)) if lens is not None else None,
+                                      _ptr(o), _ptr(lse), B, Hq, Hkv, Nk, d, float(scale), _threads(threads)),
+           "oracle_attn_decode")
+    return o, lse
 
 
 def attn_fwd_tiled(q, k, v, scale, causal=False, br=64, bc=64, trace_row=None):

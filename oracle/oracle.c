@@ -42,6 +42,10 @@
  * head's K and V; K and V are shared by G query heads, so their gradients are
  * the sums over those heads of the per-head dK and dV.
  *
+ * Decode (same page, "Implementation notes"): one query row per (batch,
+ * query head) against the first kv_len[b] keys of a key/value cache; the
+ * plain definition again, see oracle_attn_decode.
+ *
  * Parallelism: rows (forward, dQ) or keys (dK, dV) are split over POSIX
  * threads; every output element is computed by exactly one thread in a fixed
  * order, so results do not depend on the thread count.
@@ -212,6 +216,70 @@ int oracle_attn_fwd_gqa(const double* q, const double* k, const double* v, doubl
         return ORACLE_ERR_ARG;
     fwd_ctx c = {q, k, v, o, lse, N, d, scale, causal, Hq, Hq / Hkv};
     return parallel_for(B * Hq * N, nthreads, fwd_rows, &c);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode: one query row per (batch, query head) against a key/value cache   */
+/* ("FlashAttention" deep-dive page, "Implementation notes": single-query    */
+/* decode over a long cache).  The result is the plain definition: the row   */
+/* attends to the first kv_len[b] keys of its key/value head (all Nk when    */
+/* kv_len is NULL); no key visible gives O = 0 and L = -inf.                  */
+
+typedef struct {
+    const double *q, *k, *v;
+    const int64_t* kv_len;
+    double *o, *lse;
+    int64_t Hq, group, Nk, d;
+    double scale;
+} dec_ctx;
+
+static void dec_rows(void* p, int64_t begin, int64_t end) {
+    const dec_ctx* c = (const dec_ctx*)p;
+    const int64_t d = c->d;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(c->Nk > 0 ? c->Nk : 1));
+    for (int64_t r = begin; r < end; ++r) { /* r = b * Hq + h */
+        const int64_t b = r / c->Hq;
+        const int64_t n = c->kv_len ? c->kv_len[b] : c->Nk;
+        const int64_t kvh = kv_head(r, c->Hq, c->group);
+        const double* qr = c->q + r * d;
+        const double* kh = c->k + kvh * c->Nk * d;
+        const double* vh = c->v + kvh * c->Nk * d;
+        double* orow = c->o + r * d;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < n; ++j) {
+            double dot = 0.0;
+            for (int64_t t = 0; t < d; ++t) dot += qr[t] * kh[j * d + t];
+            s[j] = c->scale * dot;
+            if (s[j] > m) m = s[j];
+        }
+        for (int64_t t = 0; t < d; ++t) orow[t] = 0.0;
+        if (n == 0) {
+            c->lse[r] = -INFINITY;
+            continue;
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < n; ++j) l += exp(s[j] - m);
+        for (int64_t j = 0; j < n; ++j) {
+            const double pj = exp(s[j] - m) / l;
+            for (int64_t t = 0; t < d; ++t) orow[t] += pj * vh[j * d + t];
+        }
+        c->lse[r] = m + log(l);
+    }
+    free(s);
+}
+
+/* q, o [B, Hq, d]; lse [B, Hq]; k, v [B, Hkv, Nk, d]; kv_len [B] with
+ * 0 <= kv_len[b] <= Nk, or NULL. */
+int oracle_attn_decode(const double* q, const double* k, const double* v, const int64_t* kv_len, double* o,
+                       double* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nk, int64_t d, double scale,
+                       int nthreads) {
+    if (!q || !k || !v || !o || !lse || B <= 0 || Hq <= 0 || Hkv <= 0 || Nk <= 0 || d <= 0 || Hq % Hkv != 0)
+        return ORACLE_ERR_ARG;
+    if (kv_len)
+        for (int64_t b = 0; b < B; ++b)
+            if (kv_len[b] < 0 || kv_len[b] > Nk) return ORACLE_ERR_ARG;
+    dec_ctx c = {q, k, v, kv_len, o, lse, Hq, Hq / Hkv, Nk, d, scale};
+    return parallel_for(B * Hq, nthreads, dec_rows, &c);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -409,3 +409,72 @@ def test_gqa_backward_invariants(causal):
     np.testing.assert_allclose(dk.sum(2), 0.0, atol=1e-12)
     want = g.reshape(B, Hkv, G, N, d).sum(axis=(2, 3))
     np.testing.assert_allclose(dv.sum(2), want, atol=1e-11)
+
+
+# --- decode: one query row against a key/value cache -----------------------------
+
+def _dec_inputs(seed, B, Hq, Hkv, Nk, d):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, d))
+    k, v = (rng.standard_normal((B, Hkv, Nk, d)) for _ in range(2))
+    return q, k, v
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (4, 4), (6, 1)])
+def test_decode_against_torch_sdpa(Hq, Hkv):
+    """Each batch's row against its first kv_len[b] keys is torch's fp64
+    scaled_dot_product_attention of a length-1 query (enable_gqa); L is
+    scipy's logsumexp of the scaled scores."""
+    torch = pytest.importorskip("torch")
+    B, Nk, d = 3, 37, 8
+    q, k, v = _dec_inputs(41, B, Hq, Hkv, Nk, d)
+    lens = [37, 1, 20]
+    O, L = oracle.attn_decode(q, k, v, 0.4, kv_len=lens)
+    for b, n in enumerate(lens):
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[b:b + 1, :, None, :]), torch.from_numpy(k[b:b + 1, :, :n]),
+            torch.from_numpy(v[b:b + 1, :, :n]), scale=0.4, enable_gqa=True).numpy()[0, :, 0]
+        np.testing.assert_allclose(O[b], ref, rtol=1e-12, atol=1e-12)
+        for h in range(Hq):
+            s = 0.4 * k[b, h // (Hq // Hkv), :n] @ q[b, h]
+            np.testing.assert_allclose(L[b, h], scipy.special.logsumexp(s), rtol=1e-13, atol=1e-13)
+
+
+def test_decode_is_the_last_row_of_causal_attention():
+    """A decode step over n cached keys is the last query row of causal
+    attention over a sequence of length n (that row sees every key)."""
+    B, Hq, Hkv, n, d = 2, 4, 2, 29, 8
+    rng = np.random.default_rng(42)
+    qs = rng.standard_normal((B, Hq, n, d))
+    k, v = (rng.standard_normal((B, Hkv, n, d)) for _ in range(2))
+    Of, Lf = oracle.attn_fwd_gqa(qs, k, v, 0.3, causal=True)
+    O, L = oracle.attn_decode(np.ascontiguousarray(qs[:, :, -1]), k, v, 0.3)
+    np.testing.assert_allclose(O, Of[:, :, -1], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(L, Lf[:, :, -1], rtol=1e-13, atol=1e-14)
+
+
+def test_decode_short_caches():
+    """kv_len 0: no visible key, O = 0 and L = -inf (fully masked rows output
+    zero, deep-dive page, "Pitfalls").  kv_len 1: O = v_0 and L = scale q.k_0."""
+    q, k, v = _dec_inputs(43, 2, 3, 3, 5, 4)
+    O, L = oracle.attn_decode(q, k, v, 0.7, kv_len=[0, 1])
+    assert np.all(O[0] == 0.0) and np.all(np.isneginf(L[0]))
+    np.testing.assert_array_equal(O[1], v[1, :, 0])
+    np.testing.assert_allclose(L[1], 0.7 * np.einsum("hd,hd->h", q[1], k[1, :, 0]), rtol=1e-15)
+
+
+def test_decode_groups_read_their_own_kv_head():
+    """Grouped decode equals per-head decode with K, V repeated per query head."""
+    B, Hq, Hkv, Nk, d = 2, 6, 3, 19, 4
+    q, k, v = _dec_inputs(44, B, Hq, Hkv, Nk, d)
+    O, L = oracle.attn_decode(q, k, v, 0.5)
+    O1, L1 = oracle.attn_decode(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1), 0.5)
+    np.testing.assert_array_equal(O, O1)
+    np.testing.assert_array_equal(L, L1)
+
+
+def test_decode_rejects_bad_lengths():
+    q, k, v = _dec_inputs(45, 2, 2, 2, 5, 4)
+    for lens in ([6, 1], [-1, 2]):
+        with pytest.raises(RuntimeError):
+            oracle.attn_decode(q, k, v, 1.0, kv_len=lens)
