@@ -4,12 +4,14 @@
 One step = the whole path on one batch: fa_fwd, then the backward's four
 stages (fa_bwd_preprocess, fa_bwd_dv, fa_bwd_dk, fa_bwd_dq), on synthetic bf16 inputs
 already resident in HBM.  Default workload: causal, B=2, H=32, N=8192, d=128
-(the shape the targets are stated at), Q/K/V/dO i.i.d. N(0,1).
+(the shape the targets are stated at), Q/K/V/dO i.i.d. N(0,1).  After it, the
+split-KV decode (fa_decode) is timed on its own workload and reported under
+"decode" with its HBM roofline.
 
 Counted FLOPs: forward 4 N^2 d B H, backward 10 N^2 d B H (2.5x forward), both
 halved under a causal mask.  Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--decode NAME|none] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -27,6 +29,14 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 FL
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ("io_aware_tiled_fwd_amd/csrc/fa_fwd.hip", "io_aware_tiled_fwd_amd/csrc/fa_bwd.hip",
                   "io_aware_tiled_fwd_amd/csrc/fa_common.h")
+# Split-KV decode leg: one new token of a Llama-3-70B-like attention layer
+# (64 query heads, 8 key/value heads, d 128) at batch 1 over a 131072-token
+# cache.  name: (B, Hq, Hkv, Nk, d)
+DECODE_WORKLOADS = {
+    "decode_b1_hq64_hkv8_nk131072_d128": (1, 64, 8, 131072, 128),
+    "decode_b8_hq64_hkv8_nk32768_d128": (8, 64, 8, 32768, 128),
+}
+DEFAULT_DECODE = "decode_b1_hq64_hkv8_nk131072_d128"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_causal_b2_h32_n8192_d128.json")
 
 WORKLOADS = {
@@ -99,6 +109,48 @@ def copy_calibration(mib):
     return 0
 
 
+def decode_leg(name, iters=50, warmup=5):
+    """Time fa_decode (split kernel + merge kernel) with HIP events on the
+    launch stream; rate = compulsory bytes (K, V, q, o, L once) / mean time."""
+    import numpy as np
+    import torch
+
+    from io_aware_tiled_fwd_amd import binding, inputs
+
+    B, Hq, Hkv, Nk, d = DECODE_WORKLOADS[name]
+    ts = inputs.decode_qkv(B, Hq, Hkv, Nk, d, seed=20284, with_f64=False)
+    t = {n: torch.from_numpy(ts.bits[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ts.names}
+    del ts
+    splits, ws_bytes = binding.fa_decode_plan(B, Hq, Hkv, Nk, d)
+    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device="cuda") if ws_bytes else None
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    scale = inputs.default_scale(d)
+
+    def call():
+        binding.fa_decode(t["q"], t["k"], t["v"], o, lse, workspace=ws, scale=scale, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    mean_us = float(np.mean(ms)) * 1e3
+    nbytes = 2 * B * Hkv * Nk * d * 2 + 2 * B * Hq * d * 2 + 4 * B * Hq
+    gbs = nbytes / (mean_us / 1e6) / 1e9
+    return {"workload": name, "B": B, "Hq": Hq, "Hkv": Hkv, "Nk": Nk, "d": d, "splits": splits,
+            "us_mean": round(mean_us, 2), "us_median": round(float(np.median(ms)) * 1e3, 2),
+            "bytes_compulsory": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def cpu_baseline(heads, causal):
     """The fp64 oracle, as it stands, on host cores: forward + backward of the
     first few heads of the benchmark's own inputs (batch 0), each over all N
@@ -132,6 +184,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration)")
+    ap.add_argument("--decode", default=DEFAULT_DECODE, choices=sorted(DECODE_WORKLOADS) + ["none"],
+                    help="split-KV decode workload timed after the training step ('none' to skip)")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of batch 0 the CPU baseline computes (about 10-20 s)")
     args = ap.parse_args(argv)
@@ -244,6 +298,9 @@ def main(argv=None):
                      "traffic": recorded_traffic(dominant, args.workload)},
         "peak_bf16_tflops": PEAK_BF16_TFLOPS,
     }
+    del t, o, lse, delta, dq, dk, dv
+    if args.decode != "none":
+        out["decode"] = decode_leg(args.decode)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(cpu_heads, causal)
         out["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cb.items()

@@ -45,6 +45,7 @@
 #define FA_H
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -52,7 +53,8 @@ extern "C" {
 
 typedef enum {
     FA_OK = 0,
-    FA_ERR_INVALID_ARG = 1, /* null pointer, B/H/N < 1, Hkv not dividing Hq, non-finite scale, size overflow */
+    FA_ERR_INVALID_ARG = 1, /* null pointer, B/H/N < 1, Hkv not dividing Hq, non-finite scale, size overflow,
+                               decode workspace too small */
     FA_ERR_UNSUPPORTED = 2, /* head dimension d not in {64, 128} */
     FA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
 } fa_status;
@@ -116,6 +118,40 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dO, float* dq, float* dk, float* dv, float* delta,
                int B, int Hq, int Hkv, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Split-KV decode (Flash-Decoding): one query row per (batch, query head)
+ * against a key/value cache ("FlashAttention" deep-dive page, "Implementation
+ * notes": with a single query row, chunks of the cache are processed in
+ * parallel and their partial (m, l, acc) triples are merged with the same
+ * rescaling rule).  Grouped heads as for fa_fwd_gqa (Hkv = Hq: one key/value
+ * head per query head).
+ *   q       : const bf16 [B,Hq,d]        the new token's query rows
+ *   k, v    : const bf16 [B,Hkv,Nk,d]    the cache (Nk rows of capacity)
+ *   kv_len  : const int [B] DEVICE pointer, or NULL: batch b attends to cache
+ *             rows 0 .. kv_len[b]-1 (all Nk when NULL).  Values are clamped to
+ *             [0, Nk] on the device; kv_len[b] = 0 gives O = 0, L = -inf.
+ *   o       : bf16 [B,Hq,d]              O = softmax(scale q K^T) V per row
+ *   lse     : float [B,Hq]               natural-log logsumexp of the scaled scores
+ *   num_splits : chunks the cache is cut into; 0 lets the library choose.  The
+ *             effective count (at most ceil(Nk / 256), chunks of a multiple of
+ *             256 keys) is what fa_decode_plan reports.
+ *   workspace, workspace_bytes : device memory for the partial triples, at
+ *             least the size fa_decode_plan reports (0 bytes, and workspace may
+ *             be NULL, when the effective split count is 1).  Overwritten.
+ * The result depends on the split count only through rounding; for a fixed
+ * count it is bitwise reproducible.  Errors as for fa_fwd_gqa, plus
+ * FA_ERR_INVALID_ARG for Nk < 1, num_splits < 0, or a workspace that is NULL
+ * or smaller than required.
+ *
+ * fa_decode_plan validates the same shape arguments and reports the effective
+ * split count (*splits, may be NULL) and the workspace size in bytes
+ * (*workspace_bytes, may be NULL) for num_splits.  It launches nothing.
+ */
+int fa_decode_plan(int B, int Hq, int Hkv, int Nk, int d, int num_splits, int* splits, size_t* workspace_bytes);
+int fa_decode(const void* q, const void* k, const void* v, const int* kv_len, void* o, float* lse,
+              int B, int Hq, int Hkv, int Nk, int d, float scale, int num_splits, void* workspace,
+              size_t workspace_bytes, hipStream_t stream);
 
 /*
  * The four stages of fa_bwd, for callers that schedule or time them

@@ -21,8 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_fwd_gqa", "fa_bwd_gqa", "fa_bwd_preprocess", "fa_bwd_dv",
-           "fa_bwd_dk", "fa_bwd_dq", "fa_status_string")
+SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_fwd_gqa", "fa_bwd_gqa", "fa_decode_plan", "fa_decode",
+           "fa_bwd_preprocess", "fa_bwd_dv", "fa_bwd_dk", "fa_bwd_dq", "fa_status_string")
 
 
 class FaError(RuntimeError):
@@ -50,12 +50,14 @@ def load_library():
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
     lib.fa_fwd_gqa.argtypes = [vp] * 5 + [i, i, i, i, i, f, i, vp]
     lib.fa_bwd_gqa.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
+    lib.fa_decode_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa_decode.argtypes = [vp] * 6 + [i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
     lib.fa_bwd_preprocess.argtypes = [vp] * 3 + [i, i, i, i, vp]
     lib.fa_bwd_dv.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dk.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dq.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
-    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_bwd, lib.fa_fwd_gqa, lib.fa_bwd_gqa, lib.fa_bwd_preprocess,
-               lib.fa_bwd_dv, lib.fa_bwd_dk, lib.fa_bwd_dq):
+    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_bwd, lib.fa_fwd_gqa, lib.fa_bwd_gqa, lib.fa_decode_plan,
+               lib.fa_decode, lib.fa_bwd_preprocess, lib.fa_bwd_dv, lib.fa_bwd_dk, lib.fa_bwd_dq):
         fn.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -310,3 +312,66 @@ def attention_bwd(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):
     else:
         fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, causal, scale, stream)
     return dq, dk, dv
+
+
+def fa_decode_plan(B, Hq, Hkv, Nk, d, num_splits=0):
+    """(effective split count, workspace bytes) of a decode call."""
+    sp, ws = ctypes.c_int(0), ctypes.c_size_t(0)
+    st = load_library().fa_decode_plan(int(B), int(Hq), int(Hkv), int(Nk), int(d), int(num_splits),
+                                       ctypes.byref(sp), ctypes.byref(ws))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode_plan")
+    return sp.value, ws.value
+
+
+def _decode_shapes(q, k):
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("decode expects q [B, Hq, d] and k, v [B, Hkv, Nk, d]")
+    B, Hq, d = (int(x) for x in q.shape)
+    Hkv, Nk = int(k.shape[1]), int(k.shape[2])
+    if tuple(k.shape) != (B, Hkv, Nk, d) or Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"k must be [B, Hkv, Nk, d] with Hkv dividing Hq={Hq}")
+    return B, Hq, Hkv, Nk, d
+
+
+def fa_decode(q, k, v, o, lse, kv_len=None, num_splits=0, workspace=None, scale=None, stream=None) -> None:
+    """Split-KV decode into caller-allocated o (bf16 [B,Hq,d]) and lse (fp32
+    [B,Hq]).  q bf16 [B,Hq,d]; k, v bf16 [B,Hkv,Nk,d]; kv_len int32 [B] on the
+    device or None; workspace a device tensor of at least the bytes
+    fa_decode_plan reports (None when that is 0)."""
+    B, Hq, Hkv, Nk, d = _decode_shapes(q, k)
+    for t, n, shp in ((q, "q", (B, Hq, d)), (o, "o", (B, Hq, d)), (k, "k", (B, Hkv, Nk, d)),
+                      (v, "v", (B, Hkv, Nk, d))):
+        _check4(t, n, torch.bfloat16)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must have shape {shp}")
+    _check4(lse, "lse", torch.float32)
+    if tuple(lse.shape) != (B, Hq):
+        raise ValueError(f"lse must have shape {(B, Hq)}")
+    if kv_len is not None:
+        _check4(kv_len, "kv_len", torch.int32)
+        if tuple(kv_len.shape) != (B,):
+            raise ValueError(f"kv_len must have shape {(B,)}")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_len) if kv_len is not None else None,
+                                  _ptr(o), _ptr(lse), B, Hq, Hkv, Nk, d, sc, int(num_splits), ws_ptr, ws_bytes,
+                                  ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_decode")
+
+
+def attention_decode(q, k, v, kv_len=None, num_splits=0, scale=None, stream=None):
+    """Allocating wrapper of fa_decode: returns (o, lse); the workspace is a
+    torch allocation sized by fa_decode_plan."""
+    B, Hq, Hkv, Nk, d = _decode_shapes(q, k)
+    _, ws_bytes = fa_decode_plan(B, Hq, Hkv, Nk, d, num_splits)
+    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device=q.device) if ws_bytes else None
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    fa_decode(q, k, v, o, lse, kv_len=kv_len, num_splits=num_splits, workspace=ws, scale=scale, stream=stream)
+    return o, lse

@@ -31,6 +31,25 @@ int check_shape(int B, int H, int N, int d, float scale) {
 // Grouped heads: Hq query heads share Hkv key/value heads, Hkv dividing Hq.
 int check_groups(int Hq, int Hkv) { return (Hkv < 1 || Hq % Hkv != 0) ? FA_ERR_INVALID_ARG : FA_OK; }
 
+// Decode shapes: q [B, Hq, d], cache [B, Hkv, Nk, d].
+int check_decode(int B, int Hq, int Hkv, int Nk, int d, int num_splits) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nk < 1 || num_splits < 0) return FA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hq > INT32_MAX) return FA_ERR_INVALID_ARG;
+    // One head of the cache is addressed through a 32-bit byte range.
+    if ((double)Nk * (double)d * 2.0 > 2147483647.0) return FA_ERR_INVALID_ARG;
+    if ((double)B * (double)Hkv * (double)Nk * (double)d >= 4.611686018427388e18) return FA_ERR_INVALID_ARG;
+    // Workgroups: B * Hkv * ceil(G / 32) * splits, splits <= ceil(Nk / 256).
+    const double groups = (double)B * Hkv * (double)((Hq / Hkv + 31) / 32);
+    if (groups * (double)((Nk + 255) / 256) >= 2147483647.0) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
+size_t decode_workspace_bytes(const fa::DecodePlan& p, int B, int Hq, int d) {
+    return p.splits > 1 ? (size_t)p.splits * (size_t)B * (size_t)Hq * (size_t)(d + 2) * sizeof(float) : 0;
+}
+
 int from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 }  // namespace
@@ -123,6 +142,31 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, con
     for (const void* p : ptrs)
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
     return from_hip(fa::launch_bwd_dq(q, k, v, lse, dO, delta, dq, B, H, H, N, d, scale, causal != 0, stream));
+}
+
+int fa_decode_plan(int B, int Hq, int Hkv, int Nk, int d, int num_splits, int* splits, size_t* workspace_bytes) {
+    const int st = check_decode(B, Hq, Hkv, Nk, d, num_splits);
+    if (st != FA_OK) return st;
+    const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nk, num_splits);
+    if (splits) *splits = p.splits;
+    if (workspace_bytes) *workspace_bytes = decode_workspace_bytes(p, B, Hq, d);
+    return FA_OK;
+}
+
+int fa_decode(const void* q, const void* k, const void* v, const int* kv_len, void* o, float* lse, int B, int Hq,
+              int Hkv, int Nk, int d, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    const int st = check_decode(B, Hq, Hkv, Nk, d, num_splits);
+    if (st != FA_OK) return st;
+    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
+    if (kv_len && (reinterpret_cast<uintptr_t>(kv_len) & 3u) != 0) return FA_ERR_INVALID_ARG;
+    const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nk, num_splits);
+    const size_t need = decode_workspace_bytes(p, B, Hq, d);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return FA_ERR_INVALID_ARG;
+    return from_hip(fa::launch_decode(q, k, v, kv_len, o, lse, B, Hq, Hkv, Nk, d, scale, p,
+                                      static_cast<float*>(workspace), stream));
 }
 
 const char* fa_status_string(int status) {

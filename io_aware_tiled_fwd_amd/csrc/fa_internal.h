@@ -31,4 +31,17 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const floa
                          const float* delta, float* dq, int B, int Hq, int Hkv, int N, int d, float scale,
                          bool causal, hipStream_t stream);
 
+// Split-KV decode.  q, o [B, Hq, d], lse [B, Hq]; k, v [B, Hkv, Nk, d];
+// kv_len [B] (device, may be null).  The plan fixes the split of the cache:
+// `splits` chunks of `chunk` keys (a multiple of 256), query heads of a group
+// in `nqg` blocks of 32.  With splits > 1 the workspace holds the splits'
+// partial triples: splits * B * Hq * (d + 2) floats.
+struct DecodePlan {
+    int splits, chunk, nqg;
+};
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nk, int num_splits);
+hipError_t launch_decode(const void* q, const void* k, const void* v, const int* kv_len, void* o, float* lse, int B,
+                         int Hq, int Hkv, int Nk, int d, float scale, const DecodePlan& plan, float* workspace,
+                         hipStream_t stream);
+
 }  // namespace fa

@@ -83,6 +83,19 @@ def normal_gqa(B, Hq, Hkv, N, d, seed, with_dout=False) -> Tensors:
     return Tensors(names, "bf16", bits, f64)
 
 
+def decode_qkv(B, Hq, Hkv, Nk, d, seed, with_f64=True) -> Tensors:
+    """Decode step: Q [B, Hq, d] (one query row per head), K, V cache
+    [B, Hkv, Nk, d], i.i.d. N(0,1) from ``numpy.random.default_rng(seed)`` in
+    the order Q, K, V, stored as bf16 (``f64`` left empty unless with_f64)."""
+    rng = np.random.default_rng(seed)
+    bits, f64 = {}, {}
+    for n, shape in (("q", (B, Hq, d)), ("k", (B, Hkv, Nk, d)), ("v", (B, Hkv, Nk, d))):
+        bits[n] = bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+        if with_f64:
+            f64[n] = bf16_to_f64(bits[n])
+    return Tensors(("q", "k", "v"), "bf16", bits, f64)
+
+
 def page_generator(n, d, seed) -> np.ndarray:
     """The deterministic fp32 generator of the deep-dive page's self-test:
     element i (row-major over n x d) is ((i * 7919 + seed) mod 1000) / 500 - 1."""

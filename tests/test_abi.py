@@ -133,6 +133,55 @@ def test_gqa_rejects_bad_arguments(lib):
         assert call(ok, scale=float("nan")) == 1
 
 
+def test_decode_plan(lib):
+    """Split count and workspace size: host arithmetic only."""
+    from io_aware_tiled_fwd_amd import binding
+    # B1 Hq64 Hkv8 Nk131072 d128: automatic -> 256 workgroups / 8 groups = 32
+    # splits of 4096 keys; workspace = splits * B * Hq * (d + 2) floats.
+    assert binding.fa_decode_plan(1, 64, 8, 131072, 128) == (32, 32 * 64 * 130 * 4)
+    # short caches: splits of at least 2048 keys (1024 below 64 workgroups)
+    assert binding.fa_decode_plan(1, 64, 8, 32768, 128)[0] == 16
+    assert binding.fa_decode_plan(1, 64, 8, 8192, 128)[0] == 8
+    assert binding.fa_decode_plan(16, 32, 32, 8192, 128)[0] == 1
+    assert binding.fa_decode_plan(1, 64, 8, 131072, 128, num_splits=1) == (1, 0)
+    # at most ceil(Nk / 256) splits, chunks a multiple of 256 keys
+    assert binding.fa_decode_plan(2, 4, 4, 1000, 64, num_splits=1000) == (4, 4 * 8 * 66 * 4)
+    assert binding.fa_decode_plan(2, 4, 4, 1000, 64, num_splits=3) == (2, 2 * 8 * 66 * 4)
+    assert binding.fa_decode_plan(2, 4, 4, 1, 64) == (1, 0)
+    # G = 64 query heads per key/value head: two groups of 32 per split
+    assert binding.fa_decode_plan(1, 64, 1, 65536, 128)[0] == 32
+    for bad in ((0, 4, 4, 16, 64, 0), (1, 4, 3, 16, 64, 0), (1, 4, 4, 0, 64, 0), (1, 4, 4, 16, 64, -1)):
+        assert lib.fa_decode_plan(*bad, None, None) == 1
+    assert lib.fa_decode_plan(1, 4, 4, 16, 96, 0, None, None) == 2
+
+
+def test_decode_rejects_bad_arguments(lib):
+    """Every call here is rejected by the argument checks (no launch)."""
+    def call(ptrs, kv_len=NUL, B=1, Hq=8, Hkv=2, Nk=4096, d=128, scale=0.1, splits=4, ws=FAKE, ws_bytes=1 << 30):
+        return lib.fa_decode(*ptrs[:3], kv_len, *ptrs[3:], B, Hq, Hkv, Nk, d, ctypes.c_float(scale), splits, ws,
+                             ws_bytes, NUL)
+
+    ok = [FAKE] * 5  # q, k, v, o, lse
+    for i in range(5):
+        ptrs = list(ok)
+        ptrs[i] = NUL
+        assert call(ptrs) == 1
+    assert call(ok, B=0) == 1
+    assert call(ok, Hkv=3) == 1
+    assert call(ok, Nk=0) == 1
+    assert call(ok, d=96) == 2
+    assert call(ok, scale=float("nan")) == 1
+    assert call(ok, splits=-1) == 1
+    assert call(ok, ws=NUL) == 1                  # 4 splits need a workspace
+    assert call(ok, ws_bytes=4 * 8 * 130 * 4 - 4) == 1  # one float short
+    assert call(ok, ws=ctypes.c_void_p(0x1008)) == 1   # misaligned workspace
+    assert call(ok, kv_len=ctypes.c_void_p(0x1002), ws_bytes=0) == 1
+    ptrs = list(ok)
+    ptrs[4] = ctypes.c_void_p(0x1004)
+    assert call(ptrs, ws_bytes=0) == 1
+    assert call(ok, Nk=2 ** 24, d=128, ws_bytes=0) == 1  # one cache head over 2^31 bytes
+
+
 def test_package_import_does_not_load_library():
     import importlib
     import io_aware_tiled_fwd_amd.inputs  # noqa: F401
