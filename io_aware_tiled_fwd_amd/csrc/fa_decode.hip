@@ -245,28 +245,50 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
 }
 
 // Merge of the splits' triples, one wavefront per (batch, query head) row.
-// A split with no visible key has m = -inf and weighs 0; a row with none at
-// all gets O = 0 and L = -inf.
+// Lane s holds split s's (m, l) (64 splits per pass); the weights
+// 2^(m_s - m) reach every lane by broadcast, and the accumulator rows of 16
+// splits are requested before any is used.  A split with no visible key has
+// m = -inf and weighs 0; a row with none at all gets O = 0 and L = -inf.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_acc,
                                                            const float* __restrict__ part_ml, bf16* __restrict__ O,
                                                            float* __restrict__ LSE, int BHq, int splits) {
     constexpr int PER = D / 64;
+    constexpr int AHEAD = 16;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (row >= BHq) return;
     float mstar = -INFINITY;
-    for (int s = 0; s < splits; ++s) mstar = fmaxf(mstar, part_ml[2 * ((int64_t)s * BHq + row)]);
+    for (int s = lane; s < splits; s += 64) mstar = fmaxf(mstar, part_ml[2 * ((int64_t)s * BHq + row)]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, off));
     float acc[PER], lsum = 0.f;
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    for (int s = 0; s < splits; ++s) {
-        const int64_t prow = (int64_t)s * BHq + row;
-        const f32x2 ml = *reinterpret_cast<const f32x2*>(part_ml + 2 * prow);
-        const float wgt = ml[0] == -INFINITY ? 0.f : fast_exp2(ml[0] - mstar);
-        lsum = fmaf(wgt, ml[1], lsum);
+    for (int s0 = 0; s0 < splits; s0 += 64) {
+        float wgt = 0.f;
+        if (s0 + lane < splits) {
+            const f32x2 ml = *reinterpret_cast<const f32x2*>(part_ml + 2 * ((int64_t)(s0 + lane) * BHq + row));
+            wgt = ml[0] == -INFINITY ? 0.f : fast_exp2(ml[0] - mstar);
+            lsum = fmaf(wgt, ml[1], lsum);
+        }
+        const int n = min(64, splits - s0);
+        const float* src = part_acc + ((int64_t)s0 * BHq + row) * D + lane;
+        for (int j0 = 0; j0 < n; j0 += AHEAD) {
+            float a[AHEAD][PER];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(wgt, part_acc[prow * D + lane + 64 * e], acc[e]);
+            for (int j = 0; j < AHEAD; ++j)
+#pragma unroll
+                for (int e = 0; e < PER; ++e) a[j][e] = j0 + j < n ? src[(int64_t)(j0 + j) * BHq * D + 64 * e] : 0.f;
+#pragma unroll
+            for (int j = 0; j < AHEAD; ++j) {
+                const float wj = __shfl(wgt, j0 + j);  // 0 past the last split
+#pragma unroll
+                for (int e = 0; e < PER; ++e) acc[e] = fmaf(wj, a[j][e], acc[e]);
+            }
+        }
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
     for (int e = 0; e < PER; ++e) O[(int64_t)row * D + lane + 64 * e] = (bf16)(acc[e] * inv);
