@@ -5,8 +5,9 @@ One step = the whole path on one batch: fa_fwd, then the backward's four
 stages (fa_bwd_preprocess, fa_bwd_dv, fa_bwd_dk, fa_bwd_dq), on synthetic bf16 inputs
 already resident in HBM.  Default workload: causal, B=2, H=32, N=8192, d=128
 (the shape the targets are stated at), Q/K/V/dO i.i.d. N(0,1).  After it, the
-split-KV decode (fa_decode) is timed on its own workload and reported under
-"decode" with its HBM roofline.
+fp8 forward (fa_fwd_fp8) is timed on the same inputs quantised to e4m3
+("fwd_fp8"), and the split-KV decode (fa_decode) on its own workload
+("decode", with its HBM roofline).
 
 Counted FLOPs: forward 4 N^2 d B H, backward 10 N^2 d B H (2.5x forward), both
 halved under a causal mask.  Prints ONE JSON line.
@@ -27,6 +28,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 FLOP/clk)
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 KERNEL_SOURCES = ("io_aware_tiled_fwd_amd/csrc/fa_fwd.hip", "io_aware_tiled_fwd_amd/csrc/fa_bwd.hip",
                   "io_aware_tiled_fwd_amd/csrc/fa_common.h")
 # Split-KV decode leg: one new token of a Llama-3-70B-like attention layer
@@ -109,6 +111,44 @@ def copy_calibration(mib):
     return 0
 
 
+def fp8_leg(t, B, H, N, d, causal, scale, iters=20, warmup=3):
+    """Time fa_fwd_fp8 on the step's own Q, K, V quantised on the device to
+    OCP e4m3 with one factor per tensor (max |x| / 448); HIP events on the
+    launch stream.  FLOPs counted as for the bf16 forward."""
+    import numpy as np
+    import torch
+
+    from io_aware_tiled_fwd_amd import binding
+
+    q8, ds = {}, {}
+    for n in ("q", "k", "v"):
+        x = t[n].float()
+        ds[n] = float(x.abs().max()) / 448.0
+        q8[n] = (x / ds[n]).to(torch.float8_e4m3fn)
+        del x
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        binding.fa_fwd_fp8(q8["q"], q8["k"], q8["v"], o, lse, ds["q"], ds["k"], ds["v"], causal, scale, stream)
+
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    ff, _ = counted_flops(B, H, N, d, causal)
+    tf = ff / (ms / 1e3) / 1e12
+    return {"ms_mean": round(ms, 4), "tflops": round(tf, 2), "frac_peak_fp8": round(tf / PEAK_FP8_TFLOPS, 4),
+            "inputs": "the step's Q, K, V quantised on the device to e4m3, one factor per tensor"}
+
+
 def decode_leg(name, iters=50, warmup=5):
     """Time fa_decode (split kernel + merge kernel) with HIP events on the
     launch stream; rate = compulsory bytes (K, V, q, o, L once) / mean time."""
@@ -186,6 +226,7 @@ def main(argv=None):
                     help="only run a plain device copy of MIB MiB three times (counter calibration)")
     ap.add_argument("--decode", default=DEFAULT_DECODE, choices=sorted(DECODE_WORKLOADS) + ["none"],
                     help="split-KV decode workload timed after the training step ('none' to skip)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward leg")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of batch 0 the CPU baseline computes (about 10-20 s)")
     args = ap.parse_args(argv)
@@ -298,7 +339,10 @@ def main(argv=None):
                      "traffic": recorded_traffic(dominant, args.workload)},
         "peak_bf16_tflops": PEAK_BF16_TFLOPS,
     }
-    del t, o, lse, delta, dq, dk, dv
+    del o, lse, delta, dq, dk, dv
+    if not args.no_fp8:
+        out["fwd_fp8"] = fp8_leg(t, B, H, N, d, causal, scale)
+    del t
     if args.decode != "none":
         out["decode"] = decode_leg(args.decode)
     if not args.no_cpu_baseline:

@@ -27,7 +27,7 @@
  *    bf16 outputs are rounded to nearest, ties to even.
  *  - causal != 0 applies the square, top-left aligned mask: key j is visible to
  *    query i iff j <= i.  Tiles entirely above the diagonal are skipped.
- *  - scale is any finite float; callers usually pass 1/sqrt(d).
+ *  - scale is a finite float >= 0; callers usually pass 1/sqrt(d).
  *  - lse is the natural-log logsumexp of the SCALED scores (the value that the
  *    deep-dive page's pseudocode stores as L = m + log l).
  *  - Calls are asynchronous on `stream` (0 = the null stream); outputs are
@@ -53,8 +53,8 @@ extern "C" {
 
 typedef enum {
     FA_OK = 0,
-    FA_ERR_INVALID_ARG = 1, /* null pointer, B/H/N < 1, Hkv not dividing Hq, non-finite scale, size overflow,
-                               decode workspace too small */
+    FA_ERR_INVALID_ARG = 1, /* null pointer, B/H/N < 1, Hkv not dividing Hq, negative or non-finite scale,
+                               size overflow, decode workspace too small */
     FA_ERR_UNSUPPORTED = 2, /* head dimension d not in {64, 128} */
     FA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
 } fa_status;
@@ -77,6 +77,27 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  */
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Forward with fp8 inputs (the low-precision forward the deep-dive pages name
+ * for FlashAttention-3: "FlashAttention" deep-dive page, "Implementation
+ * notes"; "Why Flash Attention Is Fast", FlashAttention-3 section).
+ *   q, k, v : const fp8 [B,Hq,N,d] / [B,Hkv,N,d] / [B,Hkv,N,d], OCP e4m3 bytes
+ *             (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ *             infinities; 0x7F and 0xFF are NaN and must not occur)
+ *   q_descale, k_descale, v_descale : finite, > 0; the real inputs are
+ *             q_descale * q, k_descale * k, v_descale * v
+ *   o       : bf16 [B,Hq,N,d]   O = softmax(scale (q_descale q)(k_descale k)^T) (v_descale v)
+ *   lse     : float [B,Hq,N]    natural-log logsumexp of the scaled scores
+ * S is accumulated in fp32 from exact fp8 products; P is computed in fp32 and
+ * rounded to e4m3 only as the operand of the P V product, while the row sum
+ * l is taken over the unrounded P.  Grouped heads as for fa_fwd_gqa (Hkv = Hq
+ * for one key/value head per query head).  Errors as for fa_fwd_gqa, plus
+ * FA_ERR_INVALID_ARG for a factor that is not finite and positive.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int N, int d, float scale,
+               float q_descale, float k_descale, float v_descale, int causal, hipStream_t stream);
 
 /*
  * Backward, bf16 inputs, fp32 gradients.

@@ -21,8 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_fwd_gqa", "fa_bwd_gqa", "fa_decode_plan", "fa_decode",
-           "fa_bwd_preprocess", "fa_bwd_dv", "fa_bwd_dk", "fa_bwd_dq", "fa_status_string")
+SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_fwd_gqa", "fa_bwd_gqa", "fa_decode_plan",
+           "fa_decode", "fa_bwd_preprocess", "fa_bwd_dv", "fa_bwd_dk", "fa_bwd_dq", "fa_status_string")
 
 
 class FaError(RuntimeError):
@@ -50,13 +50,14 @@ def load_library():
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
     lib.fa_fwd_gqa.argtypes = [vp] * 5 + [i, i, i, i, i, f, i, vp]
     lib.fa_bwd_gqa.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_fp8.argtypes = [vp] * 5 + [i, i, i, i, i, f, f, f, f, i, vp]
     lib.fa_decode_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(ctypes.c_size_t)]
     lib.fa_decode.argtypes = [vp] * 6 + [i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
     lib.fa_bwd_preprocess.argtypes = [vp] * 3 + [i, i, i, i, vp]
     lib.fa_bwd_dv.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dk.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dq.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
-    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_bwd, lib.fa_fwd_gqa, lib.fa_bwd_gqa, lib.fa_decode_plan,
+    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_fwd_fp8, lib.fa_bwd, lib.fa_fwd_gqa, lib.fa_bwd_gqa, lib.fa_decode_plan,
                lib.fa_decode, lib.fa_bwd_preprocess, lib.fa_bwd_dv, lib.fa_bwd_dk, lib.fa_bwd_dq):
         fn.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [i]
@@ -374,4 +375,41 @@ def attention_decode(q, k, v, kv_len=None, num_splits=0, scale=None, stream=None
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     fa_decode(q, k, v, o, lse, kv_len=kv_len, num_splits=num_splits, workspace=ws, scale=scale, stream=stream)
+    return o, lse
+
+
+_FP8_DTYPES = tuple(t for t in (torch.uint8, getattr(torch, "float8_e4m3fn", None)) if t is not None)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, causal=False, scale=None, stream=None) -> None:
+    """fp8 forward: q [B,Hq,N,d], k, v [B,Hkv,N,d] holding OCP e4m3 bytes
+    (torch.float8_e4m3fn or torch.uint8), real inputs = descale * stored value;
+    into caller-allocated o (bf16 [B,Hq,N,d]) and lse (fp32 [B,Hq,N])."""
+    B, Hq, Hkv, N, d = _gqa_shapes(q, k)
+    for t, n, shp in ((q, "q", (B, Hq, N, d)), (k, "k", (B, Hkv, N, d)), (v, "v", (B, Hkv, N, d))):
+        if not isinstance(t, torch.Tensor) or t.dtype not in _FP8_DTYPES:
+            raise TypeError(f"{n} must be a float8_e4m3fn or uint8 tensor")
+        _check4(t, n, t.dtype)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must have shape {shp}")
+    _check4(o, "o", torch.bfloat16)
+    if tuple(o.shape) != (B, Hq, N, d):
+        raise ValueError(f"o must have shape {(B, Hq, N, d)}")
+    _check4(lse, "lse", torch.float32)
+    if tuple(lse.shape) != (B, Hq, N):
+        raise ValueError(f"lse must have shape {(B, Hq, N)}")
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, sc,
+                                   float(q_descale), float(k_descale), float(v_descale), int(bool(causal)),
+                                   ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
+
+
+def attention_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, scale=None, stream=None):
+    """Allocating wrapper of fa_fwd_fp8: returns (o bf16, lse fp32)."""
+    B, Hq, N, d = _shape(q)
+    o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    fa_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, causal=causal, scale=scale, stream=stream)
     return o, lse

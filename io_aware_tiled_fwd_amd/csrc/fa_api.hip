@@ -16,7 +16,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Shared shape checks.  Returns FA_OK or the status to report.
 int check_shape(int B, int H, int N, int d, float scale) {
     if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
-    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
     const int64_t bh = (int64_t)B * H;
     if (bh > INT32_MAX) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -70,6 +70,22 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
            float scale, int causal, hipStream_t stream) {
     return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, scale, causal, stream);
+}
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N, int d,
+               float scale, float q_descale, float k_descale, float v_descale, int causal, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    int st = check_shape(B, Hq, N, d, scale);
+    if (st == FA_OK) st = check_groups(Hq, Hkv);
+    if (st != FA_OK) return st;
+    const float ds[] = {q_descale, k_descale, v_descale};
+    for (float x : ds)
+        if (!isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale * q_descale * k_descale * 1.4426950408889634f)) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_INVALID_ARG;
+    return from_hip(fa::launch_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, q_descale, k_descale, v_descale,
+                                       causal != 0, stream));
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
@@ -159,7 +175,7 @@ int fa_decode(const void* q, const void* k, const void* v, const int* kv_len, vo
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
     const int st = check_decode(B, Hq, Hkv, Nk, d, num_splits);
     if (st != FA_OK) return st;
-    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
     if (kv_len && (reinterpret_cast<uintptr_t>(kv_len) & 3u) != 0) return FA_ERR_INVALID_ARG;
     const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nk, num_splits);

@@ -41,25 +41,6 @@ constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kFwdBr = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBc = 64;              // keys per tile
 
-// Map a flat workgroup id to (head, query block): XCD-contiguous task ranges
-// (see xcd_task), head-major, and within a head the heaviest query block (the
-// last, under a causal mask) first.  Returns false for padding workgroups.
-__device__ __forceinline__ bool wg_coords(int id, int BH, int nqb, bool causal, int& bh, int& qb) {
-    const int task = xcd_task(id, BH * nqb);
-    if (task >= BH * nqb) return false;
-    bh = task / nqb;
-    const int qi = task % nqb;
-    qb = causal ? (nqb - 1 - qi) : qi;
-    return true;
-}
-
-// Threshold (log2 units) by which a row's maximum must grow before the
-// accumulator is rescaled.  Any reference value m gives the same exact result
-// (O = acc / l and L = m + log2 l both carry it), so m may lag the true maximum:
-// P = 2^(S c - m) then stays below 2^8, comfortably inside fp32 and bf16 range,
-// and most key tiles skip the alpha rescale of the accumulator.
-constexpr float kRescaleThreshold = 8.0f;
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,

@@ -31,6 +31,12 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const floa
                          const float* delta, float* dq, int B, int Hq, int Hkv, int N, int d, float scale,
                          bool causal, hipStream_t stream);
 
+// Forward with fp8 (OCP e4m3) q, k, v and one dequantisation factor per
+// tensor; bf16 o, fp32 lse.  Grouped heads as for launch_fwd_bf16.
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                          int N, int d, float scale, float q_descale, float k_descale, float v_descale, bool causal,
+                          hipStream_t stream);
+
 // Split-KV decode.  q, o [B, Hq, d], lse [B, Hq]; k, v [B, Hkv, Nk, d];
 // kv_len [B] (device, may be null).  The plan fixes the split of the cache:
 // `splits` chunks of `chunk` keys (a multiple of 256), query heads of a group

@@ -13,7 +13,7 @@ the exact fp64 widening of the very values the GPU receives.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass
+from dataclasses import dataclass, field
 
 import numpy as np
 
@@ -43,11 +43,13 @@ def bf16_to_f64(bits) -> np.ndarray:
 @dataclass
 class Tensors:
     """One seeded draw.  ``bits`` holds the stored representation (uint16 bf16
-    patterns, or float32 for fp32 workloads); ``f64`` the exact widening."""
+    patterns, float32 for fp32 workloads, uint8 e4m3 bytes for fp8); ``f64``
+    the exact real values; ``descale`` the fp8 dequantisation factors."""
     names: tuple
     dtype: str
     bits: dict
     f64: dict
+    descale: dict = field(default_factory=dict)
 
 
 def normal_qkv(B, H, N, d, seed, dtype="bf16", with_dout=False) -> Tensors:
@@ -81,6 +83,59 @@ def normal_gqa(B, Hq, Hkv, N, d, seed, with_dout=False) -> Tensors:
         bits[n] = bf16_bits(rng.standard_normal((B, heads, N, d), dtype=np.float32))
         f64[n] = bf16_to_f64(bits[n])
     return Tensors(names, "bf16", bits, f64)
+
+
+def _e4m3_values() -> np.ndarray:
+    """The 256 OCP fp8 e4m3 codes as float64 (sign, 4 exponent bits with bias
+    7, 3 mantissa bits; exponent 0 is subnormal; 0x7F and 0xFF are NaN)."""
+    codes = np.arange(256)
+    sign = np.where(codes & 0x80, -1.0, 1.0)
+    e = (codes >> 3) & 0xF
+    mant = (codes & 7).astype(np.float64)
+    val = np.where(e == 0, mant / 8.0 * 2.0 ** -6, (1.0 + mant / 8.0) * 2.0 ** (e - 7.0))
+    val = sign * val
+    val[(codes & 0x7F) == 0x7F] = np.nan
+    return val
+
+
+_E4M3 = _e4m3_values()
+
+
+def e4m3_to_f64(bits) -> np.ndarray:
+    """Exact value of OCP e4m3 bytes."""
+    return _E4M3[np.asarray(bits, dtype=np.uint8)]
+
+
+def e4m3_bits(x) -> np.ndarray:
+    """Round values to OCP e4m3 (nearest, ties to the even code), saturating
+    at +-448; returns the bytes."""
+    x = np.asarray(x, dtype=np.float64)
+    pos = _E4M3[:0x7F]  # codes 0x00 .. 0x7E, ascending
+    a = np.minimum(np.abs(x), pos[-1])
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 1, len(pos) - 1)
+    lo = hi - 1
+    d_lo, d_hi = a - pos[lo], pos[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(a == 0, 0, code).astype(np.uint8)
+    return (code | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)).astype(np.uint8)
+
+
+def fp8_qkv(B, Hq, Hkv, N, d, seed) -> Tensors:
+    """Q [B, Hq, N, d], K, V [B, Hkv, N, d]: i.i.d. N(0,1) fp32 draws from
+    ``numpy.random.default_rng(seed)`` (order Q, K, V), each tensor quantised
+    to OCP e4m3 with one factor per tensor, descale = max|x| / 448 rounded to
+    fp32.  ``bits`` holds the e4m3 bytes, ``f64`` the exact real values
+    descale * e4m3, and ``descale`` the three factors."""
+    rng = np.random.default_rng(seed)
+    bits, f64, descale = {}, {}, {}
+    for n, heads in (("q", Hq), ("k", Hkv), ("v", Hkv)):
+        x = rng.standard_normal((B, heads, N, d), dtype=np.float32)
+        ds = float(np.float32(np.max(np.abs(x)) / 448.0))
+        bits[n] = e4m3_bits(x.astype(np.float64) / ds)
+        f64[n] = ds * e4m3_to_f64(bits[n])
+        descale[n] = ds
+    return Tensors(("q", "k", "v"), "fp8", bits, f64, descale)
 
 
 def decode_qkv(B, Hq, Hkv, Nk, d, seed, with_f64=True) -> Tensors:

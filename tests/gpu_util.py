@@ -15,7 +15,10 @@ TOL_BF16_GRAD = 2e-2
 
 
 def to_dev(bits, dtype):
-    """uint16 bf16 patterns or float32 values -> device tensor of that dtype."""
+    """uint16 bf16 patterns, uint8 e4m3 bytes or float32 values -> device
+    tensor (bf16, uint8 or float32)."""
+    if dtype == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint8)).to(DEV)
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
     return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.float32)).to(DEV)

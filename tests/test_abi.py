@@ -80,6 +80,7 @@ def test_fwd_rejects_bad_arguments(lib, f32):
     assert _fwd(lib, ok, N=0, f32=f32) == 1
     assert _fwd(lib, ok, scale=float("nan"), f32=f32) == 1
     assert _fwd(lib, ok, scale=float("inf"), f32=f32) == 1
+    assert _fwd(lib, ok, scale=-0.125, f32=f32) == 1  # negative scales are rejected
     assert _fwd(lib, ok, d=96, f32=f32) == 2
     assert _fwd(lib, ok, d=256, f32=f32) == 2
     assert _fwd(lib, ok, d=0, f32=f32) == 2
@@ -133,6 +134,29 @@ def test_gqa_rejects_bad_arguments(lib):
         assert call(ok, scale=float("nan")) == 1
 
 
+def test_fp8_rejects_bad_arguments(lib):
+    def call(ptrs, B=1, Hq=4, Hkv=2, N=16, d=128, scale=0.1, qd=0.01, kd=0.01, vd=0.01):
+        return lib.fa_fwd_fp8(*ptrs, B, Hq, Hkv, N, d, ctypes.c_float(scale), ctypes.c_float(qd), ctypes.c_float(kd),
+                              ctypes.c_float(vd), 1, NUL)
+
+    ok = [FAKE] * 5
+    for i in range(5):
+        ptrs = list(ok)
+        ptrs[i] = NUL
+        assert call(ptrs) == 1
+    assert call(ok, Hkv=3) == 1
+    assert call(ok, d=96) == 2
+    assert call(ok, scale=-1.0) == 1
+    for bad in (0.0, -0.5, float("nan"), float("inf")):
+        assert call(ok, qd=bad) == 1
+        assert call(ok, kd=bad) == 1
+        assert call(ok, vd=bad) == 1
+    assert call(ok, scale=1e30, qd=1e30, kd=1e30) == 1  # folded exponent scale overflows
+    ptrs = list(ok)
+    ptrs[1] = ctypes.c_void_p(0x1001)
+    assert call(ptrs) == 1
+
+
 def test_decode_plan(lib):
     """Split count and workspace size: host arithmetic only."""
     from io_aware_tiled_fwd_amd import binding
@@ -171,6 +195,7 @@ def test_decode_rejects_bad_arguments(lib):
     assert call(ok, Nk=0) == 1
     assert call(ok, d=96) == 2
     assert call(ok, scale=float("nan")) == 1
+    assert call(ok, scale=-0.5) == 1
     assert call(ok, splits=-1) == 1
     assert call(ok, ws=NUL) == 1                  # 4 splits need a workspace
     assert call(ok, ws_bytes=4 * 8 * 130 * 4 - 4) == 1  # one float short
