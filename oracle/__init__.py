@@ -19,6 +19,11 @@ Functions take and return numpy float64 arrays laid out ``[BH, N, d]``
   key/value cache of which the first ``kv_len[b]`` keys are visible (the
   single-query decode of the deep-dive page, "Implementation notes"); the plain
   definition again.
+* :func:`attn_fwd_dropout`, :func:`attn_bwd_dropout`,
+  :func:`attn_fwd_rows_dropout` -- the same with dropout of the attention
+  probabilities, the mask drawn from Philox4x32-10 by seed and offset (same
+  page, "Implementation notes"); :func:`dropout_mask` and
+  :func:`dropout_bytes` expose the mask and the generator's bytes.
 * :func:`attn_fwd_tiled` -- the per-query-block online-softmax loop of that
   page with deferred normalisation, used only to show tiled == untiled; it can
   trace the running (m, l, acc) of one row, which the worked example on the
@@ -77,6 +82,19 @@ def _load():
         lib.oracle_attn_decode.argtypes = [_f64p] * 3 + [ctypes.POINTER(_i64), _f64p, _f64p] + [_i64] * 5 + [
             ctypes.c_double, ctypes.c_int]
         lib.oracle_attn_decode.restype = ctypes.c_int
+        u64, u8p = ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint8)
+        lib.oracle_attn_fwd_dropout.argtypes = [_f64p] * 5 + [_i64] * 5 + [ctypes.c_double, ctypes.c_int,
+                                                                         ctypes.c_double, u64, u64, ctypes.c_int]
+        lib.oracle_attn_bwd_dropout.argtypes = [_f64p] * 8 + [_i64] * 5 + [ctypes.c_double, ctypes.c_int,
+                                                                         ctypes.c_double, u64, u64, ctypes.c_int]
+        lib.oracle_attn_fwd_rows_dropout.argtypes = [_f64p] * 3 + [ctypes.POINTER(_i64), _i64, _f64p, _f64p,
+                                                                   _i64, _i64, _i64, ctypes.c_double, ctypes.c_int,
+                                                                   ctypes.c_double, u64, u64, ctypes.c_int]
+        lib.oracle_dropout_mask.argtypes = [u8p, _i64, _i64, ctypes.c_double, u64, u64]
+        lib.oracle_dropout_bytes.argtypes = [u8p, _i64, _i64, u64, u64]
+        for fn in (lib.oracle_attn_fwd_dropout, lib.oracle_attn_bwd_dropout, lib.oracle_attn_fwd_rows_dropout,
+                   lib.oracle_dropout_mask, lib.oracle_dropout_bytes):
+            fn.restype = ctypes.c_int
         lib.oracle_attn_fwd_gqa.restype = ctypes.c_int
         lib.oracle_attn_bwd_gqa.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
@@ -214,6 +232,83 @@ def attn_decode(q, k, v, scale, kv_len=None, threads=0):
                                       lens.ctypes.data_as(ctypes.POINTER(_i64)) if lens is not None else None,
                                       _ptr(o), _ptr(lse), B, Hq, Hkv, Nk, d, float(scale), _threads(threads)),
            "oracle_attn_decode")
+    return o, lse
+
+
+def dropout_threshold(p):
+    """(thr, keep_scale): bytes below thr = floor(256 p + 1/2) (at most 255)
+    are dropped; kept probabilities are scaled by 256 / (256 - thr)."""
+    thr = min(255, int(np.floor(256.0 * float(p) + 0.5)))
+    return thr, 256.0 / (256.0 - thr)
+
+
+def _u8p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def dropout_mask(BH, N, p, seed, offset=0):
+    """Keep mask [BH, N, N] (uint8: 1 kept) of flat query heads, rows, keys."""
+    m = np.empty((BH, N, N), dtype=np.uint8)
+    _check(_load().oracle_dropout_mask(_u8p(m), BH, N, float(p), int(seed), int(offset)), "oracle_dropout_mask")
+    return m
+
+
+def dropout_bytes(BH, N, seed, offset=0):
+    """The Philox bytes [BH, N, N] the keep decisions compare with thr."""
+    b = np.empty((BH, N, N), dtype=np.uint8)
+    _check(_load().oracle_dropout_bytes(_u8p(b), BH, N, int(seed), int(offset)), "oracle_dropout_bytes")
+    return b
+
+
+def attn_fwd_dropout(q, k, v, scale, causal, p, seed, offset=0, threads=0):
+    """Grouped-head forward (shapes as attn_fwd_gqa) with dropout p of the
+    attention probabilities; L is that of the undropped scores."""
+    q, k, v = _as4(q, "q"), _as4(k, "k"), _as4(v, "v")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2:] != (N, d) or Hq % Hkv:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing Hq")
+    o = np.empty_like(q)
+    lse = np.empty((B, Hq, N), dtype=np.float64)
+    _check(_load().oracle_attn_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                                           float(scale), int(bool(causal)), float(p), int(seed), int(offset),
+                                           _threads(threads)), "oracle_attn_fwd_dropout")
+    return o, lse
+
+
+def attn_bwd_dropout(q, k, v, dout, scale, causal, p, seed, offset=0, threads=0):
+    """Grouped-head backward with dropout p (the forward's mask).  Returns
+    (dQ, dK, dV, D) like attn_bwd_gqa."""
+    q, k, v, dout = _as4(q, "q"), _as4(k, "k"), _as4(v, "v"), _as4(dout, "dout")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if dout.shape != q.shape or k.shape != v.shape or k.shape[0] != B or k.shape[2:] != (N, d) or Hq % Hkv:
+        raise ValueError("bad shapes for the grouped-head backward")
+    dq = np.empty_like(q)
+    dk, dv = np.empty_like(k), np.empty_like(k)
+    delta = np.empty((B, Hq, N), dtype=np.float64)
+    _check(_load().oracle_attn_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                           _ptr(delta), B, Hq, Hkv, N, d, float(scale), int(bool(causal)),
+                                           float(p), int(seed), int(offset), _threads(threads)),
+           "oracle_attn_bwd_dropout")
+    return dq, dk, dv, delta
+
+
+def attn_fwd_rows_dropout(q, k, v, rows, scale, causal, p, seed, offset=0, threads=0):
+    """attn_fwd_rows with dropout p ([BH, N, d] inputs, one key/value head per
+    query head)."""
+    q, k, v = _as3(q, "q"), _as3(k, "k"), _as3(v, "v")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must have one shape")
+    BH, N, d = q.shape
+    idx = np.ascontiguousarray(rows, dtype=np.int64)
+    o = np.empty((idx.size, d), dtype=np.float64)
+    lse = np.empty(idx.size, dtype=np.float64)
+    _check(_load().oracle_attn_fwd_rows_dropout(_ptr(q), _ptr(k), _ptr(v),
+                                                idx.ctypes.data_as(ctypes.POINTER(_i64)), idx.size, _ptr(o),
+                                                _ptr(lse), BH, N, d, float(scale), int(bool(causal)), float(p),
+                                                int(seed), int(offset), _threads(threads)),
+           "oracle_attn_fwd_rows_dropout")
     return o, lse
 
 

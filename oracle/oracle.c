@@ -117,6 +117,99 @@ static int parallel_for(int64_t count, int nthreads, range_fn fn, void* ctx) {
 static int visible(int causal, int64_t i, int64_t j) { return !causal || j <= i; }
 
 /* ------------------------------------------------------------------------ */
+/* Dropout ("FlashAttention" deep-dive page, "Implementation notes": the     */
+/* backward regenerates the mask from a Philox seed and offset).             */
+/*                                                                           */
+/* Philox4x32-10 as published by Salmon, Moraes, Dror and Shaw ("Parallel   */
+/* Random Numbers: As Easy as 1, 2, 3", SC 2011): ten rounds of              */
+/*   (c0, c1, c2, c3) -> (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, */
+/*                        lo(M0 c0))                                         */
+/* with M0 = 0xD2511F53, M1 = 0xCD9E8D57, the key (k0, k1) advanced by the    */
+/* Weyl constants (0x9E3779B9, 0xBB67AE85) before every round but the first. */
+/*                                                                           */
+/* Element (bh, i, j) -- flat query head bh, query row i, key j -- reads the */
+/* byte 8 (j mod 4) of word (j / 8) mod 4 of                                 */
+/*   Philox(counter = (2 (j / 32) + (j / 4) mod 2, i, bh, offset),           */
+/*          key = (seed mod 2^32, seed / 2^32))                              */
+/* and is kept when that byte is >= thr = floor(256 p + 1/2); kept           */
+/* probabilities are scaled by 256 / (256 - thr), so the drop probability is */
+/* thr / 256.  L and the softmax denominator are those of the undropped P.    */
+
+typedef struct {
+    int thr;           /* bytes below thr are dropped */
+    double keep_scale; /* 256 / (256 - thr) */
+    uint32_t k0, k1;   /* Philox key: the seed */
+    uint32_t offset;   /* fourth counter word */
+} dropout_cfg;
+
+static void philox4x32_10(const uint32_t ctr[4], uint32_t k0, uint32_t k1, uint32_t out[4]) {
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+static unsigned dropout_byte(const dropout_cfg* dc, int64_t bh, int64_t i, int64_t j) {
+    const uint32_t ctr[4] = {(uint32_t)(2 * (j / 32) + ((j / 4) & 1)), (uint32_t)i, (uint32_t)bh, dc->offset};
+    uint32_t w[4];
+    philox4x32_10(ctr, dc->k0, dc->k1, w);
+    return (w[(j / 8) & 3] >> (8 * (j & 3))) & 0xFFu;
+}
+
+/* The factor element (bh, i, j) of P is multiplied by: 0 (dropped) or the keep scale. */
+static double dropout_factor(const dropout_cfg* dc, int64_t bh, int64_t i, int64_t j) {
+    if (!dc) return 1.0;
+    return dropout_byte(dc, bh, i, j) >= (unsigned)dc->thr ? dc->keep_scale : 0.0;
+}
+
+static int dropout_setup(dropout_cfg* dc, double p, uint64_t seed, uint64_t offset) {
+    if (!(p >= 0.0 && p < 1.0) || offset > 0xFFFFFFFFull) return ORACLE_ERR_ARG;
+    int thr = (int)floor(256.0 * p + 0.5);
+    if (thr > 255) thr = 255;
+    dc->thr = thr;
+    dc->keep_scale = 256.0 / (256.0 - thr);
+    dc->k0 = (uint32_t)seed;
+    dc->k1 = (uint32_t)(seed >> 32);
+    dc->offset = (uint32_t)offset;
+    return ORACLE_OK;
+}
+
+/* Keep mask (1 kept, 0 dropped) of query heads bh < BH, rows i < N, keys j < N. */
+int oracle_dropout_mask(uint8_t* mask, int64_t BH, int64_t N, double p, uint64_t seed, uint64_t offset) {
+    dropout_cfg dc;
+    if (!mask || BH <= 0 || N <= 0 || dropout_setup(&dc, p, seed, offset) != ORACLE_OK) return ORACLE_ERR_ARG;
+    for (int64_t bh = 0; bh < BH; ++bh)
+        for (int64_t i = 0; i < N; ++i)
+            for (int64_t j = 0; j < N; ++j) mask[(bh * N + i) * N + j] = dropout_factor(&dc, bh, i, j) != 0.0;
+    return ORACLE_OK;
+}
+
+/* The dropout byte itself, for statistical checks of the generator. */
+int oracle_dropout_bytes(uint8_t* out, int64_t BH, int64_t N, uint64_t seed, uint64_t offset) {
+    dropout_cfg dc;
+    if (!out || BH <= 0 || N <= 0 || dropout_setup(&dc, 0.0, seed, offset) != ORACLE_OK) return ORACLE_ERR_ARG;
+    for (int64_t bh = 0; bh < BH; ++bh)
+        for (int64_t i = 0; i < N; ++i)
+            for (int64_t j = 0; j < N; ++j) out[(bh * N + i) * N + j] = (uint8_t)dropout_byte(&dc, bh, i, j);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Forward: the plain definition, one query row at a time.                   */
 
 typedef struct {
@@ -126,6 +219,7 @@ typedef struct {
     double scale;
     int causal;
     int64_t hq, group; /* query heads per batch, query heads per key/value head */
+    const dropout_cfg* drop; /* NULL: no dropout */
 } fwd_ctx;
 
 /* Key/value head (flat over batches) read by flat query head bh. */
@@ -160,7 +254,7 @@ static void fwd_one_row(const fwd_ctx* c, int64_t r, double* s, double* oi, doub
         if (visible(c->causal, i, j)) l += exp(s[j] - m);
     for (int64_t j = 0; j < N; ++j) {
         if (!visible(c->causal, i, j)) continue;
-        const double pij = exp(s[j] - m) / l;
+        const double pij = exp(s[j] - m) / l * dropout_factor(c->drop, bh, i, j);
         for (int64_t t = 0; t < d; ++t) oi[t] += pij * vh[j * d + t];
     }
     *lse_out = m + log(l);
@@ -195,14 +289,28 @@ int oracle_attn_fwd_rows(const double* q, const double* k, const double* v, cons
         return ORACLE_ERR_ARG;
     for (int64_t r = 0; r < nrows; ++r)
         if (rows[r] < 0 || rows[r] >= BH * N) return ORACLE_ERR_ARG;
-    fwd_rows_ctx c = {{q, k, v, o, lse, N, d, scale, causal, BH, 1}, rows};
+    fwd_rows_ctx c = {{q, k, v, o, lse, N, d, scale, causal, BH, 1, NULL}, rows};
+    return parallel_for(nrows, nthreads, fwd_listed_rows, &c);
+}
+
+/* oracle_attn_fwd_rows with dropout of probability p. */
+int oracle_attn_fwd_rows_dropout(const double* q, const double* k, const double* v, const int64_t* rows,
+                                 int64_t nrows, double* o, double* lse, int64_t BH, int64_t N, int64_t d,
+                                 double scale, int causal, double p, uint64_t seed, uint64_t offset, int nthreads) {
+    dropout_cfg dc;
+    if (!q || !k || !v || !rows || !o || !lse || BH <= 0 || N <= 0 || d <= 0 || nrows < 0 ||
+        dropout_setup(&dc, p, seed, offset) != ORACLE_OK)
+        return ORACLE_ERR_ARG;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= BH * N) return ORACLE_ERR_ARG;
+    fwd_rows_ctx c = {{q, k, v, o, lse, N, d, scale, causal, BH, 1, &dc}, rows};
     return parallel_for(nrows, nthreads, fwd_listed_rows, &c);
 }
 
 int oracle_attn_fwd(const double* q, const double* k, const double* v, double* o, double* lse,
                     int64_t BH, int64_t N, int64_t d, double scale, int causal, int nthreads) {
     if (!q || !k || !v || !o || !lse || BH <= 0 || N <= 0 || d <= 0) return ORACLE_ERR_ARG;
-    fwd_ctx c = {q, k, v, o, lse, N, d, scale, causal, BH, 1};
+    fwd_ctx c = {q, k, v, o, lse, N, d, scale, causal, BH, 1, NULL};
     return parallel_for(BH * N, nthreads, fwd_rows, &c);
 }
 
@@ -214,7 +322,19 @@ int oracle_attn_fwd_gqa(const double* q, const double* k, const double* v, doubl
     if (!q || !k || !v || !o || !lse || B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0 ||
         Hq % Hkv != 0)
         return ORACLE_ERR_ARG;
-    fwd_ctx c = {q, k, v, o, lse, N, d, scale, causal, Hq, Hq / Hkv};
+    fwd_ctx c = {q, k, v, o, lse, N, d, scale, causal, Hq, Hq / Hkv, NULL};
+    return parallel_for(B * Hq * N, nthreads, fwd_rows, &c);
+}
+
+/* Grouped-head forward with dropout of probability p (see dropout_cfg). */
+int oracle_attn_fwd_dropout(const double* q, const double* k, const double* v, double* o, double* lse, int64_t B,
+                            int64_t Hq, int64_t Hkv, int64_t N, int64_t d, double scale, int causal, double p,
+                            uint64_t seed, uint64_t offset, int nthreads) {
+    dropout_cfg dc;
+    if (!q || !k || !v || !o || !lse || B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || Hq % Hkv != 0 ||
+        dropout_setup(&dc, p, seed, offset) != ORACLE_OK)
+        return ORACLE_ERR_ARG;
+    fwd_ctx c = {q, k, v, o, lse, N, d, scale, causal, Hq, Hq / Hkv, &dc};
     return parallel_for(B * Hq * N, nthreads, fwd_rows, &c);
 }
 
@@ -294,6 +414,8 @@ typedef struct {
     double scale;
     int causal;
     int failed; /* set by a worker that could not allocate */
+    int64_t bh;              /* flat query head (for the dropout mask) */
+    const dropout_cfg* drop; /* NULL: no dropout */
 } bwd_ctx;
 
 /* rows i: P_i, O_i, L_i, D_i, dS_i and dQ_i */
@@ -319,29 +441,35 @@ static void bwd_rows(void* p, int64_t begin, int64_t end) {
         for (int64_t j = 0; j < N; ++j)
             Pi[j] = (m == -INFINITY || !visible(c->causal, i, j)) ? 0.0 : exp(Pi[j] - m) / l;
         c->lse[i] = (m == -INFINITY) ? -INFINITY : m + log(l);
-        /* O_i = P_i V and D_i = dO_i . O_i */
+        /* Dropout factors z_ij (0 or the keep scale; 1 without dropout), kept
+         * in dS_i until dS is formed. */
+        for (int64_t j = 0; j < N; ++j) dSi[j] = dropout_factor(c->drop, c->bh, i, j);
+        /* O_i = (P_i * z_i) V and D_i = dO_i . O_i */
         double* oi = c->o + i * d;
         for (int64_t t = 0; t < d; ++t) oi[t] = 0.0;
         for (int64_t j = 0; j < N; ++j)
-            for (int64_t t = 0; t < d; ++t) oi[t] += Pi[j] * c->v[j * d + t];
+            for (int64_t t = 0; t < d; ++t) oi[t] += Pi[j] * dSi[j] * c->v[j * d + t];
         const double* doi = c->dout + i * d;
         double Di = 0.0;
         for (int64_t t = 0; t < d; ++t) Di += doi[t] * oi[t];
         c->delta[i] = Di;
-        /* dP_ij = dO_i . v_j ; dS_ij = P_ij (dP_ij - D_i) ; dQ_i = scale sum_j dS_ij k_j */
+        /* dP_ij = dO_i . v_j ; dS_ij = P_ij (z_ij dP_ij - D_i) ; dQ_i = scale sum_j dS_ij k_j;
+         * P_i then becomes P_i * z_i, the weights of dV. */
         double* dqi = c->dq + i * d;
         for (int64_t t = 0; t < d; ++t) dqi[t] = 0.0;
         for (int64_t j = 0; j < N; ++j) {
             double dP = 0.0;
             for (int64_t t = 0; t < d; ++t) dP += doi[t] * c->v[j * d + t];
-            dSi[j] = Pi[j] * (dP - Di);
+            const double z = dSi[j];
+            dSi[j] = Pi[j] * (z * dP - Di);
+            Pi[j] *= z;
             for (int64_t t = 0; t < d; ++t) dqi[t] += dSi[j] * c->k[j * d + t];
         }
         for (int64_t t = 0; t < d; ++t) dqi[t] *= c->scale;
     }
 }
 
-/* columns j: dV_j += sum_i P_ij dO_i ; dK_j += scale sum_i dS_ij q_i (added to
+/* columns j: dV_j += sum_i (P z)_ij dO_i ; dK_j += scale sum_i dS_ij q_i (added to
  * what dv, dk hold: the key/value head may be shared by several query heads) */
 static void bwd_cols(void* p, int64_t begin, int64_t end) {
     bwd_ctx* c = (bwd_ctx*)p;
@@ -376,14 +504,15 @@ static void bwd_cols(void* p, int64_t begin, int64_t end) {
  * oracle's own fp64 O. */
 static int bwd_grouped(const double* q, const double* k, const double* v, const double* dout,
                        double* dq, double* dk, double* dv, double* delta, int64_t B, int64_t Hq,
-                       int64_t Hkv, int64_t N, int64_t d, double scale, int causal, int nthreads);
+                       int64_t Hkv, int64_t N, int64_t d, double scale, int causal, int nthreads,
+                       const dropout_cfg* drop);
 
 int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
                     double* dq, double* dk, double* dv, double* delta,
                     int64_t BH, int64_t N, int64_t d, double scale, int causal, int nthreads) {
     if (!q || !k || !v || !dout || !dq || !dk || !dv || BH <= 0 || N <= 0 || d <= 0)
         return ORACLE_ERR_ARG;
-    return bwd_grouped(q, k, v, dout, dq, dk, dv, delta, 1, BH, BH, N, d, scale, causal, nthreads);
+    return bwd_grouped(q, k, v, dout, dq, dk, dv, delta, 1, BH, BH, N, d, scale, causal, nthreads, NULL);
 }
 
 /* Grouped-head backward: q, dout, dq [B, Hq, N, d], delta [B, Hq, N],
@@ -395,12 +524,26 @@ int oracle_attn_bwd_gqa(const double* q, const double* k, const double* v, const
     if (!q || !k || !v || !dout || !dq || !dk || !dv || B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 ||
         d <= 0 || Hq % Hkv != 0)
         return ORACLE_ERR_ARG;
-    return bwd_grouped(q, k, v, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, scale, causal, nthreads);
+    return bwd_grouped(q, k, v, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, scale, causal, nthreads, NULL);
+}
+
+/* Grouped-head backward with dropout of probability p (the mask of the
+ * forward with the same seed and offset). */
+int oracle_attn_bwd_dropout(const double* q, const double* k, const double* v, const double* dout, double* dq,
+                            double* dk, double* dv, double* delta, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                            int64_t d, double scale, int causal, double p, uint64_t seed, uint64_t offset,
+                            int nthreads) {
+    dropout_cfg dc;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0 ||
+        Hq % Hkv != 0 || dropout_setup(&dc, p, seed, offset) != ORACLE_OK)
+        return ORACLE_ERR_ARG;
+    return bwd_grouped(q, k, v, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, scale, causal, nthreads, &dc);
 }
 
 static int bwd_grouped(const double* q, const double* k, const double* v, const double* dout,
                        double* dq, double* dk, double* dv, double* delta, int64_t B, int64_t Hq,
-                       int64_t Hkv, int64_t N, int64_t d, double scale, int causal, int nthreads) {
+                       int64_t Hkv, int64_t N, int64_t d, double scale, int causal, int nthreads,
+                       const dropout_cfg* drop) {
     const int64_t BH = B * Hq, group = Hq / Hkv;
     double* P = (double*)malloc(sizeof(double) * (size_t)(N * N));
     double* dS = (double*)malloc(sizeof(double) * (size_t)(N * N));
@@ -414,7 +557,7 @@ static int bwd_grouped(const double* q, const double* k, const double* v, const 
     for (int64_t bh = 0; bh < BH && rc == ORACLE_OK; ++bh) {
         const int64_t off = bh * N * d, kvoff = kv_head(bh, Hq, group) * N * d;
         bwd_ctx c = {q + off, k + kvoff, v + kvoff, dout + off, dq + off, dk + kvoff, dv + kvoff, dl,
-                     P, dS, o, lse, N, d, scale, causal, 0};
+                     P, dS, o, lse, N, d, scale, causal, 0, bh, drop};
         rc = parallel_for(N, nthreads, bwd_rows, &c);
         if (rc == ORACLE_OK) rc = parallel_for(N, nthreads, bwd_cols, &c);
         if (rc == ORACLE_OK && c.failed) rc = ORACLE_ERR_NOMEM;

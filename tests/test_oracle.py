@@ -478,3 +478,87 @@ def test_decode_rejects_bad_lengths():
     for lens in ([6, 1], [-1, 2]):
         with pytest.raises(RuntimeError):
             oracle.attn_decode(q, k, v, 1.0, kv_len=lens)
+
+
+# --- dropout (Philox mask regenerated from seed and offset) ---------------------
+
+def test_dropout_p0_is_plain_attention():
+    """p = 0 keeps every element with factor 1: forward and backward equal the
+    grouped oracle bitwise."""
+    q, k, v, g = _gqa_inputs(51, 2, 4, 2, 37, 8, with_dout=True)
+    for causal in (False, True):
+        O, L = oracle.attn_fwd_dropout(q, k, v, 0.3, causal, 0.0, seed=7)
+        O1, L1 = oracle.attn_fwd_gqa(q, k, v, 0.3, causal)
+        np.testing.assert_array_equal(O, O1)
+        np.testing.assert_array_equal(L, L1)
+        for a, b in zip(oracle.attn_bwd_dropout(q, k, v, g, 0.3, causal, 0.0, seed=7),
+                        oracle.attn_bwd_gqa(q, k, v, g, 0.3, causal)):
+            np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("p", [0.1, 0.5])
+def test_dropout_against_torch_with_the_mask(p):
+    """Given its keep mask Z, the dropout forward is softmax(S) * Z * s @ V
+    (s = 256 / (256 - thr)) and L the logsumexp of the undropped scores; the
+    backward is torch's fp64 autograd through that expression (Z constant)."""
+    torch = pytest.importorskip("torch")
+    B, Hq, Hkv, N, d = 2, 4, 2, 29, 8
+    G = Hq // Hkv
+    q, k, v, g = _gqa_inputs(52, B, Hq, Hkv, N, d, with_dout=True)
+    seed, offset = 0x1234_5678_9ABC_DEF0, 11
+    thr, ks = oracle.dropout_threshold(p)
+    Z = oracle.dropout_mask(B * Hq, N, p, seed, offset).reshape(B, Hq, N, N).astype(np.float64)
+    for causal in (False, True):
+        O, L = oracle.attn_fwd_dropout(q, k, v, 0.4, causal, p, seed, offset)
+        tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+        S = 0.4 * tq @ tk.repeat_interleave(G, dim=1).transpose(-1, -2)
+        if causal:
+            S = S.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+        P = torch.softmax(S, dim=-1)
+        Ot = (P * torch.tensor(Z) * ks) @ tv.repeat_interleave(G, dim=1)
+        np.testing.assert_allclose(O, Ot.detach().numpy(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(L, torch.logsumexp(S, dim=-1).detach().numpy(), rtol=1e-13, atol=1e-13)
+        Ot.backward(torch.tensor(g))
+        dq, dk, dv, _ = oracle.attn_bwd_dropout(q, k, v, g, 0.4, causal, p, seed, offset)
+        for got, t in zip((dq, dk, dv), (tq, tk, tv)):
+            np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_dropout_bytes_are_uniform_and_independent():
+    """The generator's bytes: chi-square of the byte histogram within 6 sigma
+    of its expectation, keep fractions within 6 binomial sigma for several p,
+    and no correlation between neighbouring rows, keys, heads, seeds and
+    offsets (the mapping gives every element its own byte)."""
+    BH, N = 8, 512
+    b = oracle.dropout_bytes(BH, N, seed=99, offset=3).astype(np.float64)
+    n = b.size
+    hist = np.bincount(b.astype(np.int64).ravel(), minlength=256)
+    chi2 = float(((hist - n / 256) ** 2 / (n / 256)).sum())
+    assert abs(chi2 - 255) < 6 * np.sqrt(2 * 255), chi2
+    for p in (1 / 256, 0.25, 0.5, 0.9):
+        thr, _ = oracle.dropout_threshold(p)
+        keep = float(oracle.dropout_mask(BH, N, p, 99, 3).mean())
+        want = 1 - thr / 256
+        assert abs(keep - want) < 6 * np.sqrt(want * (1 - want) / n), (p, keep)
+    z = (b - b.mean()) / b.std()
+
+    def corr(a, c):
+        return float((a * c).mean())
+
+    lim = 6 / np.sqrt(n / 2)
+    for shift in (1, 4, 8, 16, 32):
+        assert abs(corr(z[:, :, :-shift], z[:, :, shift:])) < lim, ("key shift", shift)
+    assert abs(corr(z[:, :-1], z[:, 1:])) < lim
+    assert abs(corr(z[:-1], z[1:])) < lim
+    for other in (oracle.dropout_bytes(BH, N, seed=100, offset=3), oracle.dropout_bytes(BH, N, seed=99, offset=4)):
+        o = other.astype(np.float64)
+        assert abs(corr(z, (o - o.mean()) / o.std())) < lim
+
+
+def test_dropout_rejects_bad_arguments():
+    q, k, v, g = _gqa_inputs(53, 1, 2, 2, 5, 4, with_dout=True)
+    for p in (-0.1, 1.0, float("nan")):
+        with pytest.raises(RuntimeError):
+            oracle.attn_fwd_dropout(q, k, v, 1.0, False, p, seed=1)
+    with pytest.raises(RuntimeError):
+        oracle.attn_fwd_dropout(q, k, v, 1.0, False, 0.1, seed=1, offset=2 ** 32)
