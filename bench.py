@@ -6,7 +6,8 @@ stages (fa_bwd_preprocess, fa_bwd_dv, fa_bwd_dk, fa_bwd_dq), on synthetic bf16 i
 already resident in HBM.  Default workload: causal, B=2, H=32, N=8192, d=128
 (the shape the targets are stated at), Q/K/V/dO i.i.d. N(0,1).  After it, the
 fp8 forward (fa_fwd_fp8) is timed on the same inputs quantised to e4m3
-("fwd_fp8"), and the split-KV decode (fa_decode) on its own workload
+("fwd_fp8"), the dropout forward and backward (p 0.1) on the same inputs
+("dropout"), and the split-KV decode (fa_decode) on its own workload
 ("decode", with its HBM roofline).
 
 Counted FLOPs: forward 4 N^2 d B H, backward 10 N^2 d B H (2.5x forward), both
@@ -149,6 +150,48 @@ def fp8_leg(t, B, H, N, d, causal, scale, iters=20, warmup=3):
             "inputs": "the step's Q, K, V quantised on the device to e4m3, one factor per tensor"}
 
 
+def dropout_leg(t, B, H, N, d, causal, scale, p=0.1, iters=10, warmup=2):
+    """Time fa_fwd_dropout and fa_bwd_dropout (dropout p, Philox mask) on the
+    step's inputs; HIP events on the launch stream; FLOPs counted as for the
+    plain step."""
+    import numpy as np
+    import torch
+
+    from io_aware_tiled_fwd_amd import binding
+
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    delta = torch.empty_like(lse)
+    dq = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+    dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        binding.fa_fwd_dropout(t["q"], t["k"], t["v"], o, lse, p, 2026, 0, causal, scale, stream)
+
+    def bwd():
+        binding.fa_bwd_dropout(t["q"], t["k"], t["v"], o, lse, t["do"], dq, dk, dv, delta, p, 2026, 0, causal,
+                               scale, stream)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(iters)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        bwd()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    fms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ff, fb = counted_flops(B, H, N, d, causal)
+    return {"p": p, "fwd_ms": round(fms, 4), "bwd_ms": round(bms, 4),
+            "fwd_tflops": round(ff / (fms / 1e3) / 1e12, 2), "bwd_tflops": round(fb / (bms / 1e3) / 1e12, 2)}
+
+
 def decode_leg(name, iters=50, warmup=5):
     """Time fa_decode (split kernel + merge kernel) with HIP events on the
     launch stream; rate = compulsory bytes (K, V, q, o, L once) / mean time."""
@@ -227,6 +270,7 @@ def main(argv=None):
     ap.add_argument("--decode", default=DEFAULT_DECODE, choices=sorted(DECODE_WORKLOADS) + ["none"],
                     help="split-KV decode workload timed after the training step ('none' to skip)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward leg")
+    ap.add_argument("--no-dropout", action="store_true", help="skip the dropout fwd+bwd leg")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of batch 0 the CPU baseline computes (about 10-20 s)")
     args = ap.parse_args(argv)
@@ -342,6 +386,8 @@ def main(argv=None):
     del o, lse, delta, dq, dk, dv
     if not args.no_fp8:
         out["fwd_fp8"] = fp8_leg(t, B, H, N, d, causal, scale)
+    if not args.no_dropout:
+        out["dropout"] = dropout_leg(t, B, H, N, d, causal, scale)
     del t
     if args.decode != "none":
         out["decode"] = decode_leg(args.decode)

@@ -79,6 +79,30 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /*
+ * Attention dropout ("FlashAttention" deep-dive page, "Implementation notes":
+ * the backward regenerates the mask from a Philox seed and offset rather than
+ * storing it).  As fa_fwd_gqa / fa_bwd_gqa, with each attention probability
+ * P_ij of flat query head bh = b*Hq + h dropped with probability thr/256 and
+ * kept ones scaled by 256/(256 - thr), thr = min(255, floor(256 dropout_p + 1/2)):
+ *   O = (P * Z) V,  Z_ij = keep_ij * 256/(256 - thr);  lse is that of the
+ *   undropped scores;  the backward uses the same Z (dS = P (Z dP - D)).
+ * keep_ij: byte 8 (j%4) of word (j/8)%4 of Philox4x32-10 (Salmon et al., SC
+ * 2011) with counter (2 (j/32) + (j/4)%2, i, bh, offset) and key (seed low
+ * 32 bits, seed high 32 bits) is >= thr.  Calls with the same seed and offset
+ * draw the same mask; fa_bwd_dropout must be given the forward's.
+ *   dropout_p : in [0, 1);  offset : below 2^32.
+ * Errors as for fa_fwd_gqa / fa_bwd_gqa, plus FA_ERR_INVALID_ARG for
+ * dropout_p outside [0, 1) or offset >= 2^32.
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                   float dropout_p, unsigned long long seed, unsigned long long offset, hipStream_t stream);
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, float* dq, float* dk, float* dv, float* delta,
+                   int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                   float dropout_p, unsigned long long seed, unsigned long long offset, hipStream_t stream);
+
+/*
  * Forward with fp8 inputs (the low-precision forward the deep-dive pages name
  * for FlashAttention-3: "FlashAttention" deep-dive page, "Implementation
  * notes"; "Why Flash Attention Is Fast", FlashAttention-3 section).

@@ -21,8 +21,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_fwd_gqa", "fa_bwd_gqa", "fa_decode_plan",
-           "fa_decode", "fa_bwd_preprocess", "fa_bwd_dv", "fa_bwd_dk", "fa_bwd_dq", "fa_status_string")
+SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_dropout",
+           "fa_bwd_dropout", "fa_decode_plan", "fa_decode", "fa_bwd_preprocess", "fa_bwd_dv", "fa_bwd_dk",
+           "fa_bwd_dq", "fa_status_string")
 
 
 class FaError(RuntimeError):
@@ -51,13 +52,16 @@ def load_library():
     lib.fa_fwd_gqa.argtypes = [vp] * 5 + [i, i, i, i, i, f, i, vp]
     lib.fa_bwd_gqa.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
     lib.fa_fwd_fp8.argtypes = [vp] * 5 + [i, i, i, i, i, f, f, f, f, i, vp]
+    ull = ctypes.c_ulonglong
+    lib.fa_fwd_dropout.argtypes = [vp] * 5 + [i, i, i, i, i, f, i, f, ull, ull, vp]
+    lib.fa_bwd_dropout.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, f, ull, ull, vp]
     lib.fa_decode_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(ctypes.c_size_t)]
     lib.fa_decode.argtypes = [vp] * 6 + [i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
     lib.fa_bwd_preprocess.argtypes = [vp] * 3 + [i, i, i, i, vp]
     lib.fa_bwd_dv.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dk.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dq.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
-    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_fwd_fp8, lib.fa_bwd, lib.fa_fwd_gqa, lib.fa_bwd_gqa, lib.fa_decode_plan,
+    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_fwd_fp8, lib.fa_fwd_dropout, lib.fa_bwd_dropout, lib.fa_bwd, lib.fa_fwd_gqa, lib.fa_bwd_gqa, lib.fa_decode_plan,
                lib.fa_decode, lib.fa_bwd_preprocess, lib.fa_bwd_dv, lib.fa_bwd_dk, lib.fa_bwd_dq):
         fn.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [i]
@@ -413,3 +417,76 @@ def attention_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False, sc
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     fa_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, causal=causal, scale=scale, stream=stream)
     return o, lse
+
+
+def _check_gqa_fwd_args(q, k, v, o, lse):
+    B, Hq, Hkv, N, d = _gqa_shapes(q, k)
+    for t, n, shp in ((q, "q", (B, Hq, N, d)), (o, "o", (B, Hq, N, d)), (k, "k", (B, Hkv, N, d)),
+                      (v, "v", (B, Hkv, N, d))):
+        _check4(t, n, torch.bfloat16)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must have shape {shp}")
+    _check4(lse, "lse", torch.float32)
+    if tuple(lse.shape) != (B, Hq, N):
+        raise ValueError(f"lse must have shape {(B, Hq, N)}")
+    return B, Hq, Hkv, N, d
+
+
+def fa_fwd_dropout(q, k, v, o, lse, dropout_p, seed, offset=0, causal=False, scale=None, stream=None) -> None:
+    """bf16 forward with attention dropout (shapes as fa_fwd_gqa): probabilities
+    are dropped with the Philox mask of (seed, offset), kept ones rescaled;
+    lse is that of the undropped scores."""
+    B, Hq, Hkv, N, d = _check_gqa_fwd_args(q, k, v, o, lse)
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d, sc,
+                                       int(bool(causal)), float(dropout_p), int(seed), int(offset),
+                                       ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_dropout")
+
+
+def fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, delta, dropout_p, seed, offset=0, causal=False, scale=None,
+                   stream=None) -> None:
+    """Backward of fa_fwd_dropout (same seed and offset), shapes as fa_bwd_gqa."""
+    B, Hq, Hkv, N, d = _gqa_shapes(q, k)
+    for t, n, shp in ((q, "q", (B, Hq, N, d)), (o, "o", (B, Hq, N, d)), (dout, "dout", (B, Hq, N, d)),
+                      (k, "k", (B, Hkv, N, d)), (v, "v", (B, Hkv, N, d))):
+        _check4(t, n, torch.bfloat16)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must have shape {shp}")
+    for t, n, shp in ((dq, "dq", (B, Hq, N, d)), (dk, "dk", (B, Hkv, N, d)), (dv, "dv", (B, Hkv, N, d))):
+        _check4(t, n, torch.float32)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must have shape {shp}")
+    for t, n in ((lse, "lse"), (delta, "delta")):
+        _check4(t, n, torch.float32)
+        if tuple(t.shape) != (B, Hq, N):
+            raise ValueError(f"{n} must have shape {(B, Hq, N)}")
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), _ptr(delta), B, Hq, Hkv, N, d, sc, int(bool(causal)),
+                                       float(dropout_p), int(seed), int(offset),
+                                       ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dropout")
+
+
+def attention_fwd_dropout(q, k, v, dropout_p, seed, offset=0, causal=False, scale=None, stream=None):
+    """Allocating wrapper of fa_fwd_dropout: returns (o, lse)."""
+    B, Hq, N, d = _shape(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    fa_fwd_dropout(q, k, v, o, lse, dropout_p, seed, offset, causal=causal, scale=scale, stream=stream)
+    return o, lse
+
+
+def attention_bwd_dropout(q, k, v, o, lse, dout, dropout_p, seed, offset=0, causal=False, scale=None, stream=None):
+    """Allocating wrapper of fa_bwd_dropout: returns (dq, dk, dv) in fp32."""
+    B, Hq, N, d = _shape(q)
+    dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty(tuple(k.shape), dtype=torch.float32, device=q.device)
+    dv = torch.empty_like(dk)
+    delta = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, delta, dropout_p, seed, offset, causal=causal, scale=scale,
+                   stream=stream)
+    return dq, dk, dv

@@ -50,6 +50,20 @@ size_t decode_workspace_bytes(const fa::DecodePlan& p, int B, int Hq, int d) {
     return p.splits > 1 ? (size_t)p.splits * (size_t)B * (size_t)Hq * (size_t)(d + 2) * sizeof(float) : 0;
 }
 
+// Dropout probability in [0, 1); the offset is one 32-bit Philox counter word.
+int check_dropout(float p, unsigned long long offset) {
+    if (!(p >= 0.f && p < 1.f) || offset > 0xFFFFFFFFull) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
+// thr = floor(256 p + 1/2) (at most 255): bytes below it are dropped.
+fa::DropoutParams dropout_params(float p, unsigned long long seed, unsigned long long offset) {
+    int thr = (int)floor(256.0 * (double)p + 0.5);
+    if (thr > 255) thr = 255;
+    return fa::DropoutParams{(uint32_t)thr, (float)(256.0 / (256.0 - thr)), (uint32_t)seed, (uint32_t)(seed >> 32),
+                             (uint32_t)offset};
+}
+
 int from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 }  // namespace
@@ -64,12 +78,43 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
     if (st != FA_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
         return FA_ERR_INVALID_ARG;
-    return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal != 0, stream));
+    return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal != 0, nullptr, stream));
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
            float scale, int causal, hipStream_t stream) {
     return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, scale, causal, stream);
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N,
+                   int d, float scale, int causal, float dropout_p, unsigned long long seed, unsigned long long offset,
+                   hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    int st = check_shape(B, Hq, N, d, scale);
+    if (st == FA_OK) st = check_groups(Hq, Hkv);
+    if (st == FA_OK) st = check_dropout(dropout_p, offset);
+    if (st != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_INVALID_ARG;
+    const fa::DropoutParams dp = dropout_params(dropout_p, seed, offset);
+    return from_hip(fa::launch_fwd_bf16(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal != 0, &dp, stream));
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                   float* dq, float* dk, float* dv, float* delta, int B, int Hq, int Hkv, int N, int d, float scale,
+                   int causal, float dropout_p, unsigned long long seed, unsigned long long offset,
+                   hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !delta) return FA_ERR_INVALID_ARG;
+    int st = check_shape(B, Hq, N, d, scale);
+    if (st == FA_OK) st = check_groups(Hq, Hkv);
+    if (st == FA_OK) st = check_dropout(dropout_p, offset);
+    if (st != FA_OK) return st;
+    const void* ptrs[] = {q, k, v, o, lse, dO, dq, dk, dv, delta};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+    const fa::DropoutParams dp = dropout_params(dropout_p, seed, offset);
+    return from_hip(fa::launch_bwd_bf16(q, k, v, o, lse, dO, dq, dk, dv, delta, B, Hq, Hkv, N, d, scale,
+                                        causal != 0, &dp, stream));
 }
 
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N, int d,
@@ -109,7 +154,7 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const
     for (const void* p : ptrs)
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
     return from_hip(fa::launch_bwd_bf16(q, k, v, o, lse, dO, dq, dk, dv, delta, B, Hq, Hkv, N, d, scale,
-                                        causal != 0, stream));
+                                        causal != 0, nullptr, stream));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
@@ -135,7 +180,7 @@ int fa_bwd_dv(const void* q, const void* k, const float* lse, const void* dO, fl
     const void* ptrs[] = {q, k, lse, dO, dv};
     for (const void* p : ptrs)
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
-    return from_hip(fa::launch_bwd_dv(q, k, lse, dO, dv, B, H, H, N, d, scale, causal != 0, stream));
+    return from_hip(fa::launch_bwd_dv(q, k, lse, dO, dv, B, H, H, N, d, scale, causal != 0, nullptr, stream));
 }
 
 int fa_bwd_dk(const void* q, const void* k, const void* v, const float* lse, const void* dO, const float* delta,
@@ -146,7 +191,7 @@ int fa_bwd_dk(const void* q, const void* k, const void* v, const float* lse, con
     const void* ptrs[] = {q, k, v, lse, dO, delta, dk};
     for (const void* p : ptrs)
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
-    return from_hip(fa::launch_bwd_dk(q, k, v, lse, dO, delta, dk, B, H, H, N, d, scale, causal != 0, stream));
+    return from_hip(fa::launch_bwd_dk(q, k, v, lse, dO, delta, dk, B, H, H, N, d, scale, causal != 0, nullptr, stream));
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO, const float* delta,
@@ -157,7 +202,7 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, con
     const void* ptrs[] = {q, k, v, lse, dO, delta, dq};
     for (const void* p : ptrs)
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
-    return from_hip(fa::launch_bwd_dq(q, k, v, lse, dO, delta, dq, B, H, H, N, d, scale, causal != 0, stream));
+    return from_hip(fa::launch_bwd_dq(q, k, v, lse, dO, delta, dq, B, H, H, N, d, scale, causal != 0, nullptr, stream));
 }
 
 int fa_decode_plan(int B, int Hq, int Hkv, int Nk, int d, int num_splits, int* splits, size_t* workspace_bytes) {

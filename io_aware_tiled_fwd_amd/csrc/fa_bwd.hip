@@ -117,11 +117,18 @@ constexpr int kDkvBkv = 32 * kBwdWaves;  // keys per workgroup
 
 // GROUPED: several query heads per key/value head (G = Hq / Hkv > 1).  Without
 // it G is the constant 1 and the group loop disappears at compile time.
-template <int D, bool CAUSAL, bool DK, bool GROUPED>
+// DROPOUT: the forward's dropout mask (fa_common.h) is regenerated.  Its
+// Philox words come per (query row, 16 keys), while a lane here holds one key
+// and 16 queries: each lane draws the words of one query row of the 32 x 32
+// tile, the keep bits of that row (one bit per key of the wavefront) go
+// through a wavefront-private LDS word, and each lane reads back the bits of
+// its key for its 16 queries.
+template <int D, bool CAUSAL, bool DK, bool GROUPED, bool DROPOUT>
 __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    float* __restrict__ dOut, int N, int BKV, int nkb, float scale_log2, float out_scale, int Hq, int G_arg) {
+    float* __restrict__ dOut, int N, int BKV, int nkb, float scale_log2, float out_scale, int Hq, int G_arg,
+    DropoutParams drop) {
     const int G = GROUPED ? G_arg : 1;
     constexpr int BQ = kDkvBq;
     constexpr int RS = both_ways_stride<D>();
@@ -129,6 +136,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(16))) bf16 sdO[2][BQ * RS];
     __shared__ __attribute__((aligned(16))) float sL[2][BQ];
     __shared__ __attribute__((aligned(16))) float sD[2][BQ];
+    __shared__ __attribute__((aligned(16))) uint32_t sKeep[DROPOUT ? kBwdWaves : 1][32];
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int lq = lane & 31, h = lane >> 5;
@@ -223,6 +231,27 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
                 const bf16* gt = sdO[buf];
 #pragma unroll
                 for (int qh = 0; qh < BQ / 32; ++qh) {
+                    // (The keep bits are formed before the score MFMAs, while
+                    // fewer accumulators are live.)
+                    uint32_t keep_bits[4];  // bit lq of word e of group r: query 32 qh + 8 r + 4 h + e kept
+                    if constexpr (DROPOUT) {
+                        // Lane (h, lq) as query row i0 + 32 qh + lq: keep bits of keys 8 a + 4 h + e.
+                        const u32x4 wd = dropout_words(drop, qh_idx, i0 + 32 * qh + lq, kw0 / 32, h);
+                        uint32_t bits = 0;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            bits |= (dropout_keep(wd, r, drop.thr) ? 1u : 0u) << (8 * (r >> 2) + 4 * h + (r & 3));
+                        const auto sw = __builtin_amdgcn_permlane32_swap(bits, bits, false, false);
+                        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                        if (h == 0) sKeep[w][lq] = sw[0] | sw[1];
+                        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const u32x4 k4 = *reinterpret_cast<const u32x4*>(&sKeep[w][8 * r + 4 * h]);
+                            keep_bits[r] = ((k4[0] >> lq) & 1u) | (((k4[1] >> lq) & 1u) << 1) |
+                                           (((k4[2] >> lq) & 1u) << 2) | (((k4[3] >> lq) & 1u) << 3);
+                        }
+                    }
                     f32x16 s = f32x16{}, dp = f32x16{};
                     if constexpr (DK) {
 #pragma unroll
@@ -260,7 +289,13 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
                             if constexpr (MASK) {
                                 if (key > i0 + 32 * qh + c_row(i, h)) p = 0.f;
                             }
-                            v[i] = DK ? p * (dp[i] - d4[e]) : p;
+                            if constexpr (DROPOUT) {
+                                const bool kept = (keep_bits[r] >> e) & 1u;
+                                if constexpr (DK) v[i] = p * ((kept ? drop.keep_scale * dp[i] : 0.f) - d4[e]);
+                                else v[i] = kept ? p : 0.f;  // the keep scale rides in out_scale
+                            } else {
+                                v[i] = DK ? p * (dp[i] - d4[e]) : p;
+                            }
                         }
                     }
                     // B operand (P for dV, dS for dK) of k-steps 0 and 1.
@@ -313,11 +348,15 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
 constexpr int kDqBq = 32 * kBwdWaves;  // query rows per workgroup
 constexpr int kDqBkv = 64;  // keys per step
 
-template <int D, bool CAUSAL>
+// DROPOUT: dS = P (z dP - D) with z the forward's dropout factor (0 or the
+// keep scale); a lane holds a query row and 16 keys per C tile, the layout
+// one Philox call covers.
+template <int D, bool CAUSAL, bool DROPOUT>
 __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    float* __restrict__ dQ, int N, int BH, int nqb, float scale_log2, float scale, int Hq, int G) {
+    float* __restrict__ dQ, int N, int BH, int nqb, float scale_log2, float scale, int Hq, int G,
+    DropoutParams drop) {
     constexpr int BKV = kDqBkv;
     constexpr int KS = both_ways_stride<D>();
     constexpr int VS = D + 8;  // rows only
@@ -395,6 +434,8 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
                                             gf[ks], dp);
                 }
                 float v[16];
+                u32x4 dw;
+                if constexpr (DROPOUT) dw = dropout_words(drop, bh, qrow, k0 / 32 + kh, h);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     float p = fast_exp2(fmaf(s[i], scale_log2, -l2));
@@ -402,7 +443,10 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
                         const int kk = k0 + 32 * kh + c_row(i, h);
                         if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
                     }
-                    v[i] = p * (dp[i] - dq_d);
+                    if constexpr (DROPOUT)
+                        v[i] = p * ((dropout_keep(dw, i, drop.thr) ? drop.keep_scale * dp[i] : 0.f) - dq_d);
+                    else
+                        v[i] = p * (dp[i] - dq_d);
                 }
                 dsf[2 * kh] = pack_bf16x8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
                 dsf[2 * kh + 1] = pack_bf16x8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
@@ -446,27 +490,47 @@ hipError_t launch_pre_t(const bf16* o, const bf16* dout, float* delta, int BH, i
     return hipGetLastError();
 }
 
+constexpr DropoutParams kNoDropout{0u, 1.f, 0u, 0u, 0u};
+
+template <int D, bool CAUSAL, bool DK, bool DROPOUT>
+hipError_t launch_dkdv_d(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
+                         const float* delta, float* out, int B, int Hq, int Hkv, int N, float scale,
+                         const DropoutParams& dp, hipStream_t stream) {
+    const int nkb = (N + kDkvBkv - 1) / kDkvBkv, BKV = B * Hkv;
+    const dim3 grid(grid_for_tasks(nkb * BKV));
+    // dV's elements carry no keep scale (kept: P, dropped: 0); it is applied on output.
+    const float out_scale = DK ? scale : (DROPOUT ? dp.keep_scale : 1.0f);
+    if (Hq == Hkv)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK, false, DROPOUT>), grid, dim3(kBwdThreads), 0, stream, q, k,
+                           v, dout, lse, delta, out, N, BKV, nkb, scale * kLog2e, out_scale, Hq, 1, dp);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK, true, DROPOUT>), grid, dim3(kBwdThreads), 0, stream, q, k,
+                           v, dout, lse, delta, out, N, BKV, nkb, scale * kLog2e, out_scale, Hq, Hq / Hkv, dp);
+    return hipGetLastError();
+}
 template <int D, bool CAUSAL, bool DK>
 hipError_t launch_dkdv_t(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
                          const float* delta, float* out, int B, int Hq, int Hkv, int N, float scale,
-                         hipStream_t stream) {
-    const int nkb = (N + kDkvBkv - 1) / kDkvBkv, BKV = B * Hkv;
-    const dim3 grid(grid_for_tasks(nkb * BKV));
-    if (Hq == Hkv)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK, false>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                           lse, delta, out, N, BKV, nkb, scale * kLog2e, DK ? scale : 1.0f, Hq, 1);
-    else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK, true>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                           lse, delta, out, N, BKV, nkb, scale * kLog2e, DK ? scale : 1.0f, Hq, Hq / Hkv);
-    return hipGetLastError();
+                         const DropoutParams* dropout, hipStream_t stream) {
+    if (dropout)
+        return launch_dkdv_d<D, CAUSAL, DK, true>(q, k, v, lse, dout, delta, out, B, Hq, Hkv, N, scale, *dropout,
+                                                  stream);
+    return launch_dkdv_d<D, CAUSAL, DK, false>(q, k, v, lse, dout, delta, out, B, Hq, Hkv, N, scale, kNoDropout,
+                                               stream);
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
-                       const float* delta, float* dq, int B, int Hq, int Hkv, int N, float scale, hipStream_t stream) {
+                       const float* delta, float* dq, int B, int Hq, int Hkv, int N, float scale,
+                       const DropoutParams* dropout, hipStream_t stream) {
     const int nqb = (N + kDqBq - 1) / kDqBq, BH = B * Hq;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(grid_for_tasks(nqb * BH)), dim3(kBwdThreads), 0, stream, q, k,
-                       v, dout, lse, delta, dq, N, BH, nqb, scale * kLog2e, scale, Hq, Hq / Hkv);
+    const dim3 grid(grid_for_tasks(nqb * BH));
+    if (dropout)
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout, lse,
+                           delta, dq, N, BH, nqb, scale * kLog2e, scale, Hq, Hq / Hkv, *dropout);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout, lse,
+                           delta, dq, N, BH, nqb, scale * kLog2e, scale, Hq, Hq / Hkv, kNoDropout);
     return hipGetLastError();
 }
 
@@ -480,11 +544,12 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, 
 }
 
 hipError_t launch_bwd_dv(const void* q, const void* k, const float* lse, const void* dout, float* dv, int B, int Hq,
-                         int Hkv, int N, int d, float scale, bool causal, hipStream_t stream) {
+                         int Hkv, int N, int d, float scale, bool causal, const DropoutParams* dropout,
+                         hipStream_t stream) {
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
     auto G = static_cast<const bf16*>(dout);
-#define FA_DV(DD, CC) launch_dkdv_t<DD, CC, false>(Q, K, K, lse, G, nullptr, dv, B, Hq, Hkv, N, scale, stream)
+#define FA_DV(DD, CC) launch_dkdv_t<DD, CC, false>(Q, K, K, lse, G, nullptr, dv, B, Hq, Hkv, N, scale, dropout, stream)
     if (d == 64) return causal ? FA_DV(64, true) : FA_DV(64, false);
     return causal ? FA_DV(128, true) : FA_DV(128, false);
 #undef FA_DV
@@ -492,12 +557,12 @@ hipError_t launch_bwd_dv(const void* q, const void* k, const float* lse, const v
 
 hipError_t launch_bwd_dk(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                          const float* delta, float* dk, int B, int Hq, int Hkv, int N, int d, float scale, bool causal,
-                         hipStream_t stream) {
+                         const DropoutParams* dropout, hipStream_t stream) {
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
     auto V = static_cast<const bf16*>(v);
     auto G = static_cast<const bf16*>(dout);
-#define FA_DK(DD, CC) launch_dkdv_t<DD, CC, true>(Q, K, V, lse, G, delta, dk, B, Hq, Hkv, N, scale, stream)
+#define FA_DK(DD, CC) launch_dkdv_t<DD, CC, true>(Q, K, V, lse, G, delta, dk, B, Hq, Hkv, N, scale, dropout, stream)
     if (d == 64) return causal ? FA_DK(64, true) : FA_DK(64, false);
     return causal ? FA_DK(128, true) : FA_DK(128, false);
 #undef FA_DK
@@ -505,12 +570,12 @@ hipError_t launch_bwd_dk(const void* q, const void* k, const void* v, const floa
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                          const float* delta, float* dq, int B, int Hq, int Hkv, int N, int d, float scale, bool causal,
-                         hipStream_t stream) {
+                         const DropoutParams* dropout, hipStream_t stream) {
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
     auto V = static_cast<const bf16*>(v);
     auto G = static_cast<const bf16*>(dout);
-#define FA_DQ(DD, CC) launch_dq_t<DD, CC>(Q, K, V, lse, G, delta, dq, B, Hq, Hkv, N, scale, stream)
+#define FA_DQ(DD, CC) launch_dq_t<DD, CC>(Q, K, V, lse, G, delta, dq, B, Hq, Hkv, N, scale, dropout, stream)
     if (d == 64) return causal ? FA_DQ(64, true) : FA_DQ(64, false);
     return causal ? FA_DQ(128, true) : FA_DQ(128, false);
 #undef FA_DQ
@@ -518,14 +583,14 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const floa
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, float* delta, int B, int Hq, int Hkv,
-                           int N, int d, float scale, bool causal, hipStream_t stream) {
+                           int N, int d, float scale, bool causal, const DropoutParams* dropout, hipStream_t stream) {
     hipError_t e = launch_bwd_preprocess(o, dout, delta, B * Hq, N, d, stream);
     if (e != hipSuccess) return e;
-    e = launch_bwd_dv(q, k, lse, dout, dv, B, Hq, Hkv, N, d, scale, causal, stream);
+    e = launch_bwd_dv(q, k, lse, dout, dv, B, Hq, Hkv, N, d, scale, causal, dropout, stream);
     if (e != hipSuccess) return e;
-    e = launch_bwd_dk(q, k, v, lse, dout, delta, dk, B, Hq, Hkv, N, d, scale, causal, stream);
+    e = launch_bwd_dk(q, k, v, lse, dout, delta, dk, B, Hq, Hkv, N, d, scale, causal, dropout, stream);
     if (e != hipSuccess) return e;
-    return launch_bwd_dq(q, k, v, lse, dout, delta, dq, B, Hq, Hkv, N, d, scale, causal, stream);
+    return launch_bwd_dq(q, k, v, lse, dout, delta, dq, B, Hq, Hkv, N, d, scale, causal, dropout, stream);
 }
 
 }  // namespace fa

@@ -120,6 +120,52 @@ constexpr float kRescaleThreshold = 8.0f;
 // query heads per batch and G query heads per key/value head.
 __device__ __forceinline__ int kv_head(int bh, int Hq, int G) { return (bh / Hq) * (Hq / G) + (bh % Hq) / G; }
 
+// Attention dropout ("FlashAttention" deep-dive page, "Implementation notes":
+// the backward regenerates the mask from a Philox seed and offset).  Element
+// (bh, i, j) -- flat query head, query row, key -- takes byte 8 (j % 4) of word
+// (j / 8) % 4 of Philox4x32-10(counter = (2 (j / 32) + (j / 4) % 2, i, bh,
+// offset), key = seed) and is kept when that byte is >= thr; kept
+// probabilities are multiplied by keep_scale = 256 / (256 - thr).  One Philox
+// call thus covers the 16 keys 32 jb + 8 a + 4 hh + e (a, e < 4) of one row:
+// exactly the keys that lane half hh holds in a 32-key C tile (c_row), with
+// register r = 4 a + e taking byte e of word a.
+struct DropoutParams {
+    uint32_t thr;       // bytes below thr are dropped
+    float keep_scale;   // 256 / (256 - thr)
+    uint32_t seed_lo, seed_hi, offset;
+};
+
+// Philox4x32-10 as published by Salmon, Moraes, Dror and Shaw ("Parallel
+// Random Numbers: As Easy as 1, 2, 3", SC 2011): ten rounds of
+// (c0, c1, c2, c3) -> (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)),
+// the key advanced by the Weyl constants before every round but the first.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+    }
+    return u32x4{c0, c1, c2, c3};
+}
+
+// The 16 dropout bytes of query row i, key block jb (32 keys), lane half hh.
+__device__ __forceinline__ u32x4 dropout_words(const DropoutParams& dp, int bh, int i, int jb, int hh) {
+    return philox4x32_10((uint32_t)(2 * jb + hh), (uint32_t)i, (uint32_t)bh, dp.offset, dp.seed_lo, dp.seed_hi);
+}
+// Whether register r's element (byte r % 4 of word r / 4) is kept.
+__device__ __forceinline__ bool dropout_keep(const u32x4& w, int r, uint32_t thr) {
+    return ((w[r >> 2] >> (8 * (r & 3))) & 0xFFu) >= thr;
+}
+
 // Buffer resource over [base, base + bytes): raw buffer loads whose byte offset
 // (VGPR offset + SGPR offset) falls outside return zero (range checking of
 // untyped buffer loads; the SGPR offset takes part, checked on hardware).  A

@@ -41,10 +41,14 @@ constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kFwdBr = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBc = 64;              // keys per tile
 
-template <int D, bool CAUSAL>
+// DROPOUT: P V uses P with the dropped elements zeroed (the dropout mask of
+// fa_common.h); l and L stay those of the undropped P, and O carries the keep
+// scale.
+template <int D, bool CAUSAL, bool DROPOUT>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, float scale_log2, int Hq, int G) {
+    bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, float scale_log2, int Hq, int G,
+    DropoutParams dp) {
     constexpr int BC = kFwdBc;
     constexpr int KS = D + 8;   // K row stride: 16 consecutive rows hit distinct banks (b128 reads)
     constexpr int VTS = BC + 8;  // V^T row stride, same property
@@ -207,6 +211,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
             const float m_use = (m == -INFINITY) ? 0.f : m;  // row with nothing visible yet
             float rs0 = 0.f, rs1 = 0.f;
             bf16x8 pf[BC / 16];
+            u32x4 dw[2];
+            if constexpr (DROPOUT) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) dw[kb] = dropout_words(dp, bh, qrow, k0 / 32 + kb, h);
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -214,8 +223,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
                     const float p = fast_exp2(fmaf(s[kb][i], scale_log2, -m_use));
                     if (i & 1) rs1 += p;
                     else rs0 += p;
+                    float pv = p;
+                    if constexpr (DROPOUT) pv = dropout_keep(dw[kb], i, dp.thr) ? p : 0.f;
                     // k-step s2 = 2 kb + i/8 covers keys 16 s2 + 8 (j/4) + 4 h + j%4, j = i%8
-                    pf[2 * kb + (i >> 3)][i & 7] = (bf16)p;
+                    pf[2 * kb + (i >> 3)][i & 7] = (bf16)pv;
                 }
             l += rs0 + rs1;
 
@@ -239,7 +250,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     // Epilogue: O = acc / l, L = (m + log2 l) ln 2.
     const float lt = pair_sum(l);
     if (qrow < N) {
-        const float inv = 1.f / lt;
+        const float inv = (DROPOUT ? dp.keep_scale : 1.f) / lt;
         bf16* op = O + base + (int64_t)qrow * D + 4 * h;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -381,7 +392,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_f32_kernel(
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                           int Hkv, int N, int d, float scale, bool causal, hipStream_t stream) {
+                           int Hkv, int N, int d, float scale, bool causal, const DropoutParams* dropout,
+                           hipStream_t stream) {
     const int BH = B * Hq, G = Hq / Hkv;
     const int nqb = (N + kFwdBr - 1) / kFwdBr;
     const int grid = grid_for_tasks(nqb * BH);
@@ -390,18 +402,25 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     auto K = static_cast<const bf16*>(k);
     auto V = static_cast<const bf16*>(v);
     auto Op = static_cast<bf16*>(o);
-#define FA_FWD_LAUNCH(DD, CC)                                                                          \
-    do {                                                                                               \
-        hipLaunchKernelGGL((fwd_bf16_kernel<DD, CC>), dim3(grid), dim3(kFwdThreads), 0, stream, Q, K, V, \
-                           Op, lse, N, BH, nqb, sl2, Hq, G);                                           \
-        return hipGetLastError();                                                                      \
+    const DropoutParams dp = dropout ? *dropout : DropoutParams{0u, 1.f, 0u, 0u, 0u};
+#define FA_FWD_LAUNCH(DD, CC, DR)                                                                          \
+    do {                                                                                                   \
+        hipLaunchKernelGGL((fwd_bf16_kernel<DD, CC, DR>), dim3(grid), dim3(kFwdThreads), 0, stream, Q, K, V, \
+                           Op, lse, N, BH, nqb, sl2, Hq, G, dp);                                           \
+        return hipGetLastError();                                                                          \
+    } while (0)
+#define FA_FWD_DROP(DD, CC)             \
+    do {                                \
+        if (dropout) FA_FWD_LAUNCH(DD, CC, true); \
+        FA_FWD_LAUNCH(DD, CC, false);   \
     } while (0)
     if (d == 64) {
-        if (causal) FA_FWD_LAUNCH(64, true);
-        FA_FWD_LAUNCH(64, false);
+        if (causal) FA_FWD_DROP(64, true);
+        FA_FWD_DROP(64, false);
     }
-    if (causal) FA_FWD_LAUNCH(128, true);
-    FA_FWD_LAUNCH(128, false);
+    if (causal) FA_FWD_DROP(128, true);
+    FA_FWD_DROP(128, false);
+#undef FA_FWD_DROP
 #undef FA_FWD_LAUNCH
 }
 

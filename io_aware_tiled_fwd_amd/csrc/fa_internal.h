@@ -6,30 +6,36 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include "fa_common.h"
+
 namespace fa {
 
-// Forward, bf16 in/out.  d in {64, 128}.
+// Forward, bf16 in/out.  d in {64, 128}.  dropout: null for none.
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                           int Hkv, int N, int d, float scale, bool causal, hipStream_t stream);
+                           int Hkv, int N, int d, float scale, bool causal, const DropoutParams* dropout,
+                           hipStream_t stream);
 // Forward, fp32 in/out (one key/value head per query head).
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
                           int N, int d, float scale, bool causal, hipStream_t stream);
 // Backward: preprocess (delta), dV, dK and dQ kernels, in stream order.
+// dropout: null for none, else the forward's mask is regenerated.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, float* delta, int B, int Hq,
-                           int Hkv, int N, int d, float scale, bool causal, hipStream_t stream);
+                           int Hkv, int N, int d, float scale, bool causal, const DropoutParams* dropout,
+                           hipStream_t stream);
 
 // The backward's stages, individually.
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int BHq, int N, int d,
                                  hipStream_t stream);
 hipError_t launch_bwd_dv(const void* q, const void* k, const float* lse, const void* dout, float* dv, int B,
-                         int Hq, int Hkv, int N, int d, float scale, bool causal, hipStream_t stream);
+                         int Hq, int Hkv, int N, int d, float scale, bool causal, const DropoutParams* dropout,
+                         hipStream_t stream);
 hipError_t launch_bwd_dk(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                          const float* delta, float* dk, int B, int Hq, int Hkv, int N, int d, float scale,
-                         bool causal, hipStream_t stream);
+                         bool causal, const DropoutParams* dropout, hipStream_t stream);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                          const float* delta, float* dq, int B, int Hq, int Hkv, int N, int d, float scale,
-                         bool causal, hipStream_t stream);
+                         bool causal, const DropoutParams* dropout, hipStream_t stream);
 
 // Forward with fp8 (OCP e4m3) q, k, v and one dequantisation factor per
 // tensor; bf16 o, fp32 lse.  Grouped heads as for launch_fwd_bf16.

@@ -157,6 +157,29 @@ def test_fp8_rejects_bad_arguments(lib):
     assert call(ptrs) == 1
 
 
+def test_dropout_rejects_bad_arguments(lib):
+    def fwd(ptrs, p=0.1, offset=0, Hq=4, Hkv=2, d=128, scale=0.1):
+        return lib.fa_fwd_dropout(*ptrs, 1, Hq, Hkv, 16, d, ctypes.c_float(scale), 1, ctypes.c_float(p), 7, offset,
+                                  NUL)
+
+    def bwd(ptrs, p=0.1, offset=0, Hq=4, Hkv=2, d=128, scale=0.1):
+        return lib.fa_bwd_dropout(*ptrs, 1, Hq, Hkv, 16, d, ctypes.c_float(scale), 1, ctypes.c_float(p), 7, offset,
+                                  NUL)
+
+    for call, n in ((fwd, 5), (bwd, 10)):
+        ok = [FAKE] * n
+        for i in range(n):
+            ptrs = list(ok)
+            ptrs[i] = NUL
+            assert call(ptrs) == 1
+        for p in (-0.01, 1.0, 1.5, float("nan")):
+            assert call(ok, p=p) == 1
+        assert call(ok, offset=2 ** 32) == 1
+        assert call(ok, Hkv=3) == 1
+        assert call(ok, d=96) == 2
+        assert call(ok, scale=-1.0) == 1
+
+
 def test_decode_plan(lib):
     """Split count and workspace size: host arithmetic only."""
     from io_aware_tiled_fwd_amd import binding
