@@ -23,7 +23,10 @@ Functions take and return numpy float64 arrays laid out ``[BH, N, d]``
   :func:`attn_fwd_rows_dropout` -- the same with dropout of the attention
   probabilities, the mask drawn from Philox4x32-10 by seed and offset (same
   page, "Implementation notes"); :func:`dropout_mask` and
-  :func:`dropout_bytes` expose the mask and the generator's bytes.
+  :func:`dropout_bytes` expose the mask and the generator's bytes.  The
+  generator's exact output bits are parity unpinned (no published vector in
+  the pages; its statistics and the dropout arithmetic given the mask are
+  pinned).
 * :func:`attn_fwd_tiled` -- the per-query-block online-softmax loop of that
   page with deferred normalisation, used only to show tiled == untiled; it can
   trace the running (m, l, acc) of one row, which the worked example on the

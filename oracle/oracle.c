@@ -134,6 +134,8 @@ static int visible(int causal, int64_t i, int64_t j) { return !causal || j <= i;
 /* and is kept when that byte is >= thr = floor(256 p + 1/2); kept           */
 /* probabilities are scaled by 256 / (256 - thr), so the drop probability is */
 /* thr / 256.  L and the softmax denominator are those of the undropped P.    */
+/* The generator's exact output bits are parity unpinned: the pages print no */
+/* Philox vector (its statistics and the dropout arithmetic are pinned).     */
 
 typedef struct {
     int thr;           /* bytes below thr are dropped */
