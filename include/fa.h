@@ -165,6 +165,15 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const
                int B, int Hq, int Hkv, int N, int d, float scale, int causal, hipStream_t stream);
 
 /*
+ * fa_bwd_gqa with bf16 gradients: dq, dk, dv are bf16 (round to nearest even
+ * of the fp32 accumulators) instead of fp32; everything else as fa_bwd_gqa.
+ * Halves the gradients' HBM writes for callers that keep gradients in bf16.
+ */
+int fa_bwd_gqa_bf16grad(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dO, void* dq, void* dk, void* dv, float* delta,
+                        int B, int Hq, int Hkv, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
  * Split-KV decode (Flash-Decoding): one query row per (batch, query head)
  * against a key/value cache ("FlashAttention" deep-dive page, "Implementation
  * notes": with a single query row, chunks of the cache are processed in

@@ -21,7 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_dropout",
+SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_fwd_gqa", "fa_bwd_gqa", "fa_bwd_gqa_bf16grad",
+           "fa_fwd_dropout",
            "fa_bwd_dropout", "fa_decode_plan", "fa_decode", "fa_bwd_preprocess", "fa_bwd_dv", "fa_bwd_dk",
            "fa_bwd_dq", "fa_status_string")
 
@@ -53,6 +54,7 @@ def load_library():
     lib.fa_bwd_gqa.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
     lib.fa_fwd_fp8.argtypes = [vp] * 5 + [i, i, i, i, i, f, f, f, f, i, vp]
     ull = ctypes.c_ulonglong
+    lib.fa_bwd_gqa_bf16grad.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
     lib.fa_fwd_dropout.argtypes = [vp] * 5 + [i, i, i, i, i, f, i, f, ull, ull, vp]
     lib.fa_bwd_dropout.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, f, ull, ull, vp]
     lib.fa_decode_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(ctypes.c_size_t)]
@@ -61,7 +63,8 @@ def load_library():
     lib.fa_bwd_dv.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dk.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dq.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
-    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_fwd_fp8, lib.fa_fwd_dropout, lib.fa_bwd_dropout, lib.fa_bwd, lib.fa_fwd_gqa, lib.fa_bwd_gqa, lib.fa_decode_plan,
+    for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_fwd_fp8, lib.fa_fwd_dropout, lib.fa_bwd_dropout,
+               lib.fa_bwd_gqa_bf16grad, lib.fa_bwd, lib.fa_fwd_gqa, lib.fa_bwd_gqa, lib.fa_decode_plan,
                lib.fa_decode, lib.fa_bwd_preprocess, lib.fa_bwd_dv, lib.fa_bwd_dk, lib.fa_bwd_dq):
         fn.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [i]
@@ -490,3 +493,24 @@ def attention_bwd_dropout(q, k, v, o, lse, dout, dropout_p, seed, offset=0, caus
     fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, delta, dropout_p, seed, offset, causal=causal, scale=scale,
                    stream=stream)
     return dq, dk, dv
+
+
+def fa_bwd_gqa_bf16grad(q, k, v, o, lse, dout, dq, dk, dv, delta, causal=False, scale=None, stream=None) -> None:
+    """fa_bwd_gqa with bf16 dq [B,Hq,N,d] and dk, dv [B,Hkv,N,d]."""
+    B, Hq, Hkv, N, d = _gqa_shapes(q, k)
+    for t, n, shp in ((q, "q", (B, Hq, N, d)), (o, "o", (B, Hq, N, d)), (dout, "dout", (B, Hq, N, d)),
+                      (k, "k", (B, Hkv, N, d)), (v, "v", (B, Hkv, N, d)), (dq, "dq", (B, Hq, N, d)),
+                      (dk, "dk", (B, Hkv, N, d)), (dv, "dv", (B, Hkv, N, d))):
+        _check4(t, n, torch.bfloat16)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must have shape {shp}")
+    for t, n in ((lse, "lse"), (delta, "delta")):
+        _check4(t, n, torch.float32)
+        if tuple(t.shape) != (B, Hq, N):
+            raise ValueError(f"{n} must have shape {(B, Hq, N)}")
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_bwd_gqa_bf16grad(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                            _ptr(dk), _ptr(dv), _ptr(delta), B, Hq, Hkv, N, d, sc, int(bool(causal)),
+                                            ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_gqa_bf16grad")

@@ -114,7 +114,7 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
     const fa::DropoutParams dp = dropout_params(dropout_p, seed, offset);
     return from_hip(fa::launch_bwd_bf16(q, k, v, o, lse, dO, dq, dk, dv, delta, B, Hq, Hkv, N, d, scale,
-                                        causal != 0, &dp, stream));
+                                        causal != 0, &dp, false, stream));
 }
 
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N, int d,
@@ -154,7 +154,21 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const
     for (const void* p : ptrs)
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
     return from_hip(fa::launch_bwd_bf16(q, k, v, o, lse, dO, dq, dk, dv, delta, B, Hq, Hkv, N, d, scale,
-                                        causal != 0, nullptr, stream));
+                                        causal != 0, nullptr, false, stream));
+}
+
+int fa_bwd_gqa_bf16grad(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                        void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv, int N, int d, float scale,
+                        int causal, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !delta) return FA_ERR_INVALID_ARG;
+    int st = check_shape(B, Hq, N, d, scale);
+    if (st == FA_OK) st = check_groups(Hq, Hkv);
+    if (st != FA_OK) return st;
+    const void* ptrs[] = {q, k, v, o, lse, dO, dq, dk, dv, delta};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+    return from_hip(fa::launch_bwd_bf16(q, k, v, o, lse, dO, dq, dk, dv, delta, B, Hq, Hkv, N, d, scale,
+                                        causal != 0, nullptr, true, stream));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
@@ -180,7 +194,7 @@ int fa_bwd_dv(const void* q, const void* k, const float* lse, const void* dO, fl
     const void* ptrs[] = {q, k, lse, dO, dv};
     for (const void* p : ptrs)
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
-    return from_hip(fa::launch_bwd_dv(q, k, lse, dO, dv, B, H, H, N, d, scale, causal != 0, nullptr, stream));
+    return from_hip(fa::launch_bwd_dv(q, k, lse, dO, dv, B, H, H, N, d, scale, causal != 0, nullptr, false, stream));
 }
 
 int fa_bwd_dk(const void* q, const void* k, const void* v, const float* lse, const void* dO, const float* delta,
@@ -191,7 +205,8 @@ int fa_bwd_dk(const void* q, const void* k, const void* v, const float* lse, con
     const void* ptrs[] = {q, k, v, lse, dO, delta, dk};
     for (const void* p : ptrs)
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
-    return from_hip(fa::launch_bwd_dk(q, k, v, lse, dO, delta, dk, B, H, H, N, d, scale, causal != 0, nullptr, stream));
+    return from_hip(
+        fa::launch_bwd_dk(q, k, v, lse, dO, delta, dk, B, H, H, N, d, scale, causal != 0, nullptr, false, stream));
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO, const float* delta,
@@ -202,7 +217,8 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, con
     const void* ptrs[] = {q, k, v, lse, dO, delta, dq};
     for (const void* p : ptrs)
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
-    return from_hip(fa::launch_bwd_dq(q, k, v, lse, dO, delta, dq, B, H, H, N, d, scale, causal != 0, nullptr, stream));
+    return from_hip(
+        fa::launch_bwd_dq(q, k, v, lse, dO, delta, dq, B, H, H, N, d, scale, causal != 0, nullptr, false, stream));
 }
 
 int fa_decode_plan(int B, int Hq, int Hkv, int Nk, int d, int num_splits, int* splits, size_t* workspace_bytes) {

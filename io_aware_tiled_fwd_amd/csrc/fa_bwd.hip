@@ -112,6 +112,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_preprocess_kernel(const bf16*
 //      dK: dP = dO V^T       (A = dO rows from LDS, B = V^T from registers)
 //          dS = P (dP - D);  dK^T += Q^T dS  (A = Q^T: transposing reads; B = dS)
 
+// Gradient stores: fp32, or bf16 rounded to nearest even.
+__device__ __forceinline__ void store_grad4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void store_grad4(bf16* p, f32x4 v) {
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+
 constexpr int kDkvBq = 64;    // query rows per step
 constexpr int kDkvBkv = 32 * kBwdWaves;  // keys per workgroup
 
@@ -123,11 +129,12 @@ constexpr int kDkvBkv = 32 * kBwdWaves;  // keys per workgroup
 // tile, the keep bits of that row (one bit per key of the wavefront) go
 // through a wavefront-private LDS word, and each lane reads back the bits of
 // its key for its 16 queries.
-template <int D, bool CAUSAL, bool DK, bool GROUPED, bool DROPOUT>
+// OutT: float or bf16 gradient output.
+template <int D, bool CAUSAL, bool DK, bool GROUPED, bool DROPOUT, typename OutT>
 __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    float* __restrict__ dOut, int N, int BKV, int nkb, float scale_log2, float out_scale, int Hq, int G_arg,
+    OutT* __restrict__ dOut, int N, int BKV, int nkb, float scale_log2, float out_scale, int Hq, int G_arg,
     DropoutParams drop) {
     const int G = GROUPED ? G_arg : 1;
     constexpr int BQ = kDkvBq;
@@ -325,14 +332,14 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
 
     // Register i of block db holds dim 32 db + c_row(i, h) of this lane's key.
     if (key < N) {
-        float* op = dOut + base + (int64_t)key * D + 4 * h;
+        OutT* op = dOut + base + (int64_t)key * D + 4 * h;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                *reinterpret_cast<f32x4*>(op + 32 * db + 8 * r) =
-                    f32x4{acc[db][4 * r] * out_scale, acc[db][4 * r + 1] * out_scale, acc[db][4 * r + 2] * out_scale,
-                          acc[db][4 * r + 3] * out_scale};
+                store_grad4(op + 32 * db + 8 * r,
+                            f32x4{acc[db][4 * r] * out_scale, acc[db][4 * r + 1] * out_scale,
+                                  acc[db][4 * r + 2] * out_scale, acc[db][4 * r + 3] * out_scale});
     }
 }
 
@@ -351,11 +358,11 @@ constexpr int kDqBkv = 64;  // keys per step
 // DROPOUT: dS = P (z dP - D) with z the forward's dropout factor (0 or the
 // keep scale); a lane holds a query row and 16 keys per C tile, the layout
 // one Philox call covers.
-template <int D, bool CAUSAL, bool DROPOUT>
+template <int D, bool CAUSAL, bool DROPOUT, typename OutT>
 __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    float* __restrict__ dQ, int N, int BH, int nqb, float scale_log2, float scale, int Hq, int G,
+    OutT* __restrict__ dQ, int N, int BH, int nqb, float scale_log2, float scale, int Hq, int G,
     DropoutParams drop) {
     constexpr int BKV = kDqBkv;
     constexpr int KS = both_ways_stride<D>();
@@ -469,14 +476,14 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
     for (int j = j_split; j < ntiles; ++j) step(j, std::true_type{});
 
     if (qrow < N) {
-        float* dqp = dQ + base + (int64_t)qrow * D + 4 * h;
+        OutT* dqp = dQ + base + (int64_t)qrow * D + 4 * h;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                *reinterpret_cast<f32x4*>(dqp + 32 * db + 8 * r) =
-                    f32x4{dqacc[db][4 * r] * scale, dqacc[db][4 * r + 1] * scale, dqacc[db][4 * r + 2] * scale,
-                          dqacc[db][4 * r + 3] * scale};
+                store_grad4(dqp + 32 * db + 8 * r,
+                            f32x4{dqacc[db][4 * r] * scale, dqacc[db][4 * r + 1] * scale,
+                                  dqacc[db][4 * r + 2] * scale, dqacc[db][4 * r + 3] * scale});
     }
 }
 
@@ -492,45 +499,55 @@ hipError_t launch_pre_t(const bf16* o, const bf16* dout, float* delta, int BH, i
 
 constexpr DropoutParams kNoDropout{0u, 1.f, 0u, 0u, 0u};
 
-template <int D, bool CAUSAL, bool DK, bool DROPOUT>
+template <int D, bool CAUSAL, bool DK, bool DROPOUT, typename OutT>
 hipError_t launch_dkdv_d(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
-                         const float* delta, float* out, int B, int Hq, int Hkv, int N, float scale,
+                         const float* delta, OutT* out, int B, int Hq, int Hkv, int N, float scale,
                          const DropoutParams& dp, hipStream_t stream) {
     const int nkb = (N + kDkvBkv - 1) / kDkvBkv, BKV = B * Hkv;
     const dim3 grid(grid_for_tasks(nkb * BKV));
     // dV's elements carry no keep scale (kept: P, dropped: 0); it is applied on output.
     const float out_scale = DK ? scale : (DROPOUT ? dp.keep_scale : 1.0f);
     if (Hq == Hkv)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK, false, DROPOUT>), grid, dim3(kBwdThreads), 0, stream, q, k,
-                           v, dout, lse, delta, out, N, BKV, nkb, scale * kLog2e, out_scale, Hq, 1, dp);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK, false, DROPOUT, OutT>), grid, dim3(kBwdThreads), 0, stream,
+                           q, k, v, dout, lse, delta, out, N, BKV, nkb, scale * kLog2e, out_scale, Hq, 1, dp);
     else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK, true, DROPOUT>), grid, dim3(kBwdThreads), 0, stream, q, k,
-                           v, dout, lse, delta, out, N, BKV, nkb, scale * kLog2e, out_scale, Hq, Hq / Hkv, dp);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK, true, DROPOUT, OutT>), grid, dim3(kBwdThreads), 0, stream,
+                           q, k, v, dout, lse, delta, out, N, BKV, nkb, scale * kLog2e, out_scale, Hq, Hq / Hkv, dp);
     return hipGetLastError();
 }
+// out: fp32, or bf16 when grad_bf16 (bf16 gradients have no dropout variant).
 template <int D, bool CAUSAL, bool DK>
 hipError_t launch_dkdv_t(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
-                         const float* delta, float* out, int B, int Hq, int Hkv, int N, float scale,
-                         const DropoutParams* dropout, hipStream_t stream) {
+                         const float* delta, void* out, int B, int Hq, int Hkv, int N, float scale,
+                         const DropoutParams* dropout, bool grad_bf16, hipStream_t stream) {
+    if (grad_bf16)
+        return launch_dkdv_d<D, CAUSAL, DK, false>(q, k, v, lse, dout, delta, static_cast<bf16*>(out), B, Hq, Hkv, N,
+                                                   scale, kNoDropout, stream);
     if (dropout)
-        return launch_dkdv_d<D, CAUSAL, DK, true>(q, k, v, lse, dout, delta, out, B, Hq, Hkv, N, scale, *dropout,
-                                                  stream);
-    return launch_dkdv_d<D, CAUSAL, DK, false>(q, k, v, lse, dout, delta, out, B, Hq, Hkv, N, scale, kNoDropout,
-                                               stream);
+        return launch_dkdv_d<D, CAUSAL, DK, true>(q, k, v, lse, dout, delta, static_cast<float*>(out), B, Hq, Hkv, N,
+                                                  scale, *dropout, stream);
+    return launch_dkdv_d<D, CAUSAL, DK, false>(q, k, v, lse, dout, delta, static_cast<float*>(out), B, Hq, Hkv, N,
+                                               scale, kNoDropout, stream);
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
-                       const float* delta, float* dq, int B, int Hq, int Hkv, int N, float scale,
-                       const DropoutParams* dropout, hipStream_t stream) {
+                       const float* delta, void* dq, int B, int Hq, int Hkv, int N, float scale,
+                       const DropoutParams* dropout, bool grad_bf16, hipStream_t stream) {
     const int nqb = (N + kDqBq - 1) / kDqBq, BH = B * Hq;
     const dim3 grid(grid_for_tasks(nqb * BH));
-    if (dropout)
-        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout, lse,
-                           delta, dq, N, BH, nqb, scale * kLog2e, scale, Hq, Hq / Hkv, *dropout);
+    if (grad_bf16)
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, bf16>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout,
+                           lse, delta, static_cast<bf16*>(dq), N, BH, nqb, scale * kLog2e, scale, Hq, Hq / Hkv,
+                           kNoDropout);
+    else if (dropout)
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true, float>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout,
+                           lse, delta, static_cast<float*>(dq), N, BH, nqb, scale * kLog2e, scale, Hq, Hq / Hkv,
+                           *dropout);
     else
-        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout, lse,
-                           delta, dq, N, BH, nqb, scale * kLog2e, scale, Hq, Hq / Hkv, kNoDropout);
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, float>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout,
+                           lse, delta, static_cast<float*>(dq), N, BH, nqb, scale * kLog2e, scale, Hq, Hq / Hkv,
+                           kNoDropout);
     return hipGetLastError();
 }
 
@@ -543,54 +560,57 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, 
     return d == 64 ? launch_pre_t<64>(Op, G, delta, BHq, N, stream) : launch_pre_t<128>(Op, G, delta, BHq, N, stream);
 }
 
-hipError_t launch_bwd_dv(const void* q, const void* k, const float* lse, const void* dout, float* dv, int B, int Hq,
-                         int Hkv, int N, int d, float scale, bool causal, const DropoutParams* dropout,
+hipError_t launch_bwd_dv(const void* q, const void* k, const float* lse, const void* dout, void* dv, int B, int Hq,
+                         int Hkv, int N, int d, float scale, bool causal, const DropoutParams* dropout, bool grad_bf16,
                          hipStream_t stream) {
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
     auto G = static_cast<const bf16*>(dout);
-#define FA_DV(DD, CC) launch_dkdv_t<DD, CC, false>(Q, K, K, lse, G, nullptr, dv, B, Hq, Hkv, N, scale, dropout, stream)
+#define FA_DV(DD, CC) \
+    launch_dkdv_t<DD, CC, false>(Q, K, K, lse, G, nullptr, dv, B, Hq, Hkv, N, scale, dropout, grad_bf16, stream)
     if (d == 64) return causal ? FA_DV(64, true) : FA_DV(64, false);
     return causal ? FA_DV(128, true) : FA_DV(128, false);
 #undef FA_DV
 }
 
 hipError_t launch_bwd_dk(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                         const float* delta, float* dk, int B, int Hq, int Hkv, int N, int d, float scale, bool causal,
-                         const DropoutParams* dropout, hipStream_t stream) {
+                         const float* delta, void* dk, int B, int Hq, int Hkv, int N, int d, float scale, bool causal,
+                         const DropoutParams* dropout, bool grad_bf16, hipStream_t stream) {
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
     auto V = static_cast<const bf16*>(v);
     auto G = static_cast<const bf16*>(dout);
-#define FA_DK(DD, CC) launch_dkdv_t<DD, CC, true>(Q, K, V, lse, G, delta, dk, B, Hq, Hkv, N, scale, dropout, stream)
+#define FA_DK(DD, CC) \
+    launch_dkdv_t<DD, CC, true>(Q, K, V, lse, G, delta, dk, B, Hq, Hkv, N, scale, dropout, grad_bf16, stream)
     if (d == 64) return causal ? FA_DK(64, true) : FA_DK(64, false);
     return causal ? FA_DK(128, true) : FA_DK(128, false);
 #undef FA_DK
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                         const float* delta, float* dq, int B, int Hq, int Hkv, int N, int d, float scale, bool causal,
-                         const DropoutParams* dropout, hipStream_t stream) {
+                         const float* delta, void* dq, int B, int Hq, int Hkv, int N, int d, float scale, bool causal,
+                         const DropoutParams* dropout, bool grad_bf16, hipStream_t stream) {
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
     auto V = static_cast<const bf16*>(v);
     auto G = static_cast<const bf16*>(dout);
-#define FA_DQ(DD, CC) launch_dq_t<DD, CC>(Q, K, V, lse, G, delta, dq, B, Hq, Hkv, N, scale, dropout, stream)
+#define FA_DQ(DD, CC) launch_dq_t<DD, CC>(Q, K, V, lse, G, delta, dq, B, Hq, Hkv, N, scale, dropout, grad_bf16, stream)
     if (d == 64) return causal ? FA_DQ(64, true) : FA_DQ(64, false);
     return causal ? FA_DQ(128, true) : FA_DQ(128, false);
 #undef FA_DQ
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                           const void* dout, float* dq, float* dk, float* dv, float* delta, int B, int Hq, int Hkv,
-                           int N, int d, float scale, bool causal, const DropoutParams* dropout, hipStream_t stream) {
+                           const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv,
+                           int N, int d, float scale, bool causal, const DropoutParams* dropout, bool grad_bf16,
+                           hipStream_t stream) {
     hipError_t e = launch_bwd_preprocess(o, dout, delta, B * Hq, N, d, stream);
     if (e != hipSuccess) return e;
-    e = launch_bwd_dv(q, k, lse, dout, dv, B, Hq, Hkv, N, d, scale, causal, dropout, stream);
+    e = launch_bwd_dv(q, k, lse, dout, dv, B, Hq, Hkv, N, d, scale, causal, dropout, grad_bf16, stream);
     if (e != hipSuccess) return e;
-    e = launch_bwd_dk(q, k, v, lse, dout, delta, dk, B, Hq, Hkv, N, d, scale, causal, dropout, stream);
+    e = launch_bwd_dk(q, k, v, lse, dout, delta, dk, B, Hq, Hkv, N, d, scale, causal, dropout, grad_bf16, stream);
     if (e != hipSuccess) return e;
-    return launch_bwd_dq(q, k, v, lse, dout, delta, dq, B, Hq, Hkv, N, d, scale, causal, dropout, stream);
+    return launch_bwd_dq(q, k, v, lse, dout, delta, dq, B, Hq, Hkv, N, d, scale, causal, dropout, grad_bf16, stream);
 }
 
 }  // namespace fa

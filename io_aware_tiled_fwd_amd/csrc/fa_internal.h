@@ -19,23 +19,24 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           int N, int d, float scale, bool causal, hipStream_t stream);
 // Backward: preprocess (delta), dV, dK and dQ kernels, in stream order.
 // dropout: null for none, else the forward's mask is regenerated.
+// grad_bf16: dq, dk, dv are bf16 (no dropout then), else fp32.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                           const void* dout, float* dq, float* dk, float* dv, float* delta, int B, int Hq,
+                           const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int Hq,
                            int Hkv, int N, int d, float scale, bool causal, const DropoutParams* dropout,
-                           hipStream_t stream);
+                           bool grad_bf16, hipStream_t stream);
 
 // The backward's stages, individually.
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int BHq, int N, int d,
                                  hipStream_t stream);
-hipError_t launch_bwd_dv(const void* q, const void* k, const float* lse, const void* dout, float* dv, int B,
+hipError_t launch_bwd_dv(const void* q, const void* k, const float* lse, const void* dout, void* dv, int B,
                          int Hq, int Hkv, int N, int d, float scale, bool causal, const DropoutParams* dropout,
-                         hipStream_t stream);
+                         bool grad_bf16, hipStream_t stream);
 hipError_t launch_bwd_dk(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                         const float* delta, float* dk, int B, int Hq, int Hkv, int N, int d, float scale,
-                         bool causal, const DropoutParams* dropout, hipStream_t stream);
+                         const float* delta, void* dk, int B, int Hq, int Hkv, int N, int d, float scale,
+                         bool causal, const DropoutParams* dropout, bool grad_bf16, hipStream_t stream);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                         const float* delta, float* dq, int B, int Hq, int Hkv, int N, int d, float scale,
-                         bool causal, const DropoutParams* dropout, hipStream_t stream);
+                         const float* delta, void* dq, int B, int Hq, int Hkv, int N, int d, float scale,
+                         bool causal, const DropoutParams* dropout, bool grad_bf16, hipStream_t stream);
 
 // Forward with fp8 (OCP e4m3) q, k, v and one dequantisation factor per
 // tensor; bf16 o, fp32 lse.  Grouped heads as for launch_fwd_bf16.

@@ -119,7 +119,10 @@ def test_gqa_rejects_bad_arguments(lib):
     def bwd(ptrs, B=1, Hq=4, Hkv=2, N=16, d=128, scale=0.1):
         return lib.fa_bwd_gqa(*ptrs, B, Hq, Hkv, N, d, ctypes.c_float(scale), 1, NUL)
 
-    for call, n in ((fwd, 5), (bwd, 10)):
+    def bwd16(ptrs, B=1, Hq=4, Hkv=2, N=16, d=128, scale=0.1):
+        return lib.fa_bwd_gqa_bf16grad(*ptrs, B, Hq, Hkv, N, d, ctypes.c_float(scale), 1, NUL)
+
+    for call, n in ((fwd, 5), (bwd, 10), (bwd16, 10)):
         ok = [FAKE] * n
         for i in range(n):
             ptrs = list(ok)

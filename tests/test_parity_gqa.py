@@ -80,3 +80,27 @@ def test_gqa_matches_repeated_heads():
     for got, per_head in ((dk, dk1), (dv, dv1)):
         summed = per_head.reshape(B, Hkv, G, N, d).sum(2)
         assert maxabs(f64(got), f64(summed)) <= 1e-4
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_gradients(Hq, Hkv, d):
+    """fa_bwd_gqa_bf16grad stores the same fp32 accumulators rounded to bf16
+    (nearest even): bitwise the fp32-gradient path's results rounded, and
+    within the bf16 bar of the oracle."""
+    for N, causal in ((129, True), (300, False), (1000, True)):
+        ts = inputs.normal_gqa(2, Hq, Hkv, N, d, 1100 + N, with_dout=True)
+        scale = inputs.default_scale(d)
+        dev, o, lse, (dq, dk, dv) = _run(ts, causal, scale)
+        dq16, dk16, dv16 = (torch.empty(t.shape, dtype=torch.bfloat16, device="cuda") for t in (dq, dk, dv))
+        delta = torch.empty_like(lse)
+        binding.fa_bwd_gqa_bf16grad(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], dq16, dk16, dv16, delta,
+                                    causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        for got, full in ((dq16, dq), (dk16, dk), (dv16, dv)):
+            assert torch.equal(got, full.to(torch.bfloat16))
+        rq, rk, rv, _ = oracle.attn_bwd_gqa(ts.f64["q"], ts.f64["k"], ts.f64["v"], ts.f64["do"], scale, causal)
+        what = f"bf16 grads Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal}"
+        _check(what + " dQ", dq16, rq, TOL_BF16_GRAD)
+        _check(what + " dK", dk16, rk, TOL_BF16_GRAD)
+        _check(what + " dV", dv16, rv, TOL_BF16_GRAD)
