@@ -110,7 +110,7 @@ def _load():
 
 def default_threads() -> int:
     """Threads the oracle uses by default: the CPUs this process may run on,
-    capped by OMP_NUM_THREADS when that is set (a GPU machine's CPU share)."""
+    capped by OMP_NUM_THREADS when that is set (a share of a shared host)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
