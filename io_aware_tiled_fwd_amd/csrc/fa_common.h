@@ -11,7 +11,7 @@
 // Every kernel computes the TRANSPOSED score tile S^T = K Q^T so that one lane
 // column is one query row: a row's statistics live in one lane and its partner
 // lane l^32, and the output accumulator O^T = V^T P^T takes P^T straight from
-// the score registers (see the key-slot permutation in the forward kernel).
+// the score registers (the transposing reads below deliver V^T in their k order).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -213,13 +213,5 @@ __device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
 
 // Row (key or query) held by register i of lane half h in a 32x32 C tile.
 __device__ __forceinline__ constexpr int c_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
-
-// Key-slot permutation inside each group of 16 keys: swap bits 2 and 3.
-// The P^T operand of k-step s (16 keys) is taken from score registers whose
-// keys are 16s + 8*(j/4) + 4h + j%4; storing V^T at slot(key) makes those eight
-// keys contiguous (slots 16s + 8h + j), so one 16-byte LDS read feeds V^T.
-__device__ __forceinline__ constexpr int key_slot(int key) {
-    return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
 
 }  // namespace fa

@@ -16,15 +16,14 @@
 // one workgroup of 8 wavefronts per (batch*head, block of 256 query rows);
 // each wavefront owns 32 query rows, so no softmax statistic is ever shared
 // between wavefronts.  Each key tile of 64 keys is staged once in LDS, double
-// buffered, and read by all eight wavefronts (two per SIMD):
-//   K   row-major [64 keys][d]   -> A operand of S^T = K Q^T
-//   V^T row-major [d][64 keys]   -> A operand of O^T = V^T P^T
-// Both are read as 16-byte rows.  V^T is produced while staging: each wave
-// multiplies a 32-key block of V by identity operands on the MFMA unit
-// (exact: every product is x * 1 or x * 0), which leaves one dimension's keys
-// per lane, and writes them in the key order of the P^T registers (key_slot).
-// Global loads for tile j+1 are issued into registers before tile j is
-// computed and land in the other LDS buffers afterwards: one barrier per tile.
+// buffered, and read by all eight wavefronts (two per SIMD), both tensors as
+// plain row-major copies [64 keys][d]:
+//   K  16-byte row reads                -> A operand of S^T = K Q^T
+//   V  transposing reads (lds_read_tr_a) -> A operand V^T of O^T = V^T P^T
+// The transposing read returns keys in the k order of the P^T registers
+// (16 s + 8 (j/4) + 4 h + j%4), so P needs no shuffle.  Global loads for tile
+// j+1 are issued into registers before tile j is computed and land in the
+// other LDS buffers afterwards: one barrier per tile.
 //
 // Latency: the K fragments of S are read four MFMAs ahead, and the V^T
 // fragments of the first two k-steps of O^T are read right after S, so that
@@ -51,7 +50,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     DropoutParams dp) {
     constexpr int BC = kFwdBc;
     constexpr int KS = D + 8;   // K row stride: 16 consecutive rows hit distinct banks (b128 reads)
-    constexpr int VTS = BC + 8;  // V^T row stride, same property
+    constexpr int VS = D + 32;   // V rows, read transposed: 4 rows x 64 B of a half wave on disjoint banks
     constexpr int DCH = D / 8;  // 16-byte chunks per row
     constexpr int CH = BC * DCH / kFwdThreads;  // K chunks per thread
     static_assert(CH * kFwdThreads == BC * DCH, "tile split");
@@ -60,7 +59,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     constexpr int NPRE = 2;      // k-steps of O^T whose V^T fragments are read early
 
     __shared__ __attribute__((aligned(16))) bf16 sK[2][BC * KS];
-    __shared__ __attribute__((aligned(16))) bf16 sVt[2][D * VTS];
+    __shared__ __attribute__((aligned(16))) bf16 sV[2][BC * VS];
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int lq = lane & 31, h = lane >> 5;
@@ -98,53 +97,28 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     // half-blocks of 32 keys x 16 dimensions, HB consecutive ones per wave; a
     // lane loads V[32 vkb + lq][16 vd16 + 8 h .. +7] of each, the MFMA operand
     // A of C = V I.  Tile offsets ride in the scalar offset.
-    constexpr int HB = D / 64;
     constexpr int ROWS_PER_PASS = kFwdThreads / DCH;
     const int ld_off = ((tid / DCH) * D + 8 * (tid % DCH)) * 2;
-    const int vkb = (w * HB) / (D / 16), vd16 = (w * HB) % (D / 16);
-    const int va_off = ((32 * vkb + lq) * D + 16 * vd16 + 8 * h) * 2;
-    // Identity operands: I1[k][n] = (n == k), I2[k][n] = (n == k + 16); lane l holds k = 8 h + j, n = lq.
-    bf16x8 id1, id2;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        id1[j] = (bf16)(lq == 8 * h + j ? 1.f : 0.f);
-        id2[j] = (bf16)(lq == 16 + 8 * h + j ? 1.f : 0.f);
-    }
-    u32x4 kreg[CH];
-    bf16x8 va[HB];
+    u32x4 kreg[CH], vreg[CH];
     auto load_tile = [&](int j) {
         const int soff = j * BC * D * 2;
 #pragma unroll
         for (int r = 0; r < CH; ++r) kreg[r] = buffer_load16(krs, ld_off + r * ROWS_PER_PASS * D * 2, soff);
 #pragma unroll
-        for (int t = 0; t < HB; ++t) va[t] = __builtin_bit_cast(bf16x8, buffer_load16(vrs, va_off + 32 * t, soff));
+        for (int r = 0; r < CH; ++r) vreg[r] = buffer_load16(vrs, ld_off + r * ROWS_PER_PASS * D * 2, soff);
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int r = 0; r < CH; ++r) {
             const int c = tid + kFwdThreads * r;
             *reinterpret_cast<u32x4*>(&sK[buf][(c / DCH) * KS + 8 * (c % DCH)]) = kreg[r];
-        }
-        // C[key][n] = V[32 vkb + key][16 vd16 + n]: register 4 r + c of lane
-        // (h, lq) holds key 8 r + 4 h + c of dimension 16 vd16 + lq, and keys
-        // 4 apart land in contiguous key slots.
-        f32x16 t = mfma_bf16_32x32x16(va[0], id1, f32x16{});
-        if constexpr (HB == 2) t = mfma_bf16_32x32x16(va[1], id2, t);
-        if (HB == 2 || lq < 16) {
-            bf16* dst = &sVt[buf][(16 * vd16 + lq) * VTS + 32 * vkb + 8 * h];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bf16x2 lo = __builtin_convertvector(f32x2{t[4 * r], t[4 * r + 1]}, bf16x2);
-                const bf16x2 hi = __builtin_convertvector(f32x2{t[4 * r + 2], t[4 * r + 3]}, bf16x2);
-                *reinterpret_cast<u32x2*>(dst + 16 * (r >> 1) + 4 * (r & 1)) =
-                    u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-            }
+            *reinterpret_cast<u32x4*>(&sV[buf][(c / DCH) * VS + 8 * (c % DCH)]) = vreg[r];
         }
     };
 
     // Per-lane offsets of the K rows and the V^T rows.
     const int k_off = lq * KS + 8 * h;
-    const int v_off = lq * VTS + 8 * h;
+    const int v_off = tr_row(lane) * VS + tr_col(lane);
 
     // Loads and stores are unconditional (the last iteration re-reads the final
     // tile into the idle buffer): every path then drains the load counter at the
@@ -160,7 +134,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
         // Skip tiles entirely above this wave's diagonal (a scalar branch).
         if (!CAUSAL || __builtin_amdgcn_readfirstlane(k0 <= qw0 + 31)) {
             const bf16* kt = sK[buf];
-            const bf16* vt = sVt[buf];
+            const bf16* vt = sV[buf];
             if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
             // S^T = K Q^T for two 32-key halves, the two accumulation chains interleaved.
             f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -185,7 +159,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
             for (int s2 = 0; s2 < NPRE; ++s2)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) vpre[s2][db] = lds_read16_early(vt + 32 * db * VTS + v_off + 16 * s2);
+                for (int db = 0; db < NDB; ++db) vpre[s2][db] = lds_read_tr_a(vt + 16 * s2 * VS + v_off + 32 * db, VS);
 
             // Mask keys past N and, on tiles crossing the diagonal, keys after the query.
             if (k0 + BC > N || (CAUSAL && k0 + BC - 1 > qw0)) {
@@ -237,7 +211,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const bf16x8 vf = s2 < NPRE ? vpre[s2 < NPRE ? s2 : 0][db]
-                                                : *reinterpret_cast<const bf16x8*>(vt + 32 * db * VTS + v_off + 16 * s2);
+                                                : lds_read_tr_a(vt + 16 * s2 * VS + v_off + 32 * db, VS);
                     oacc[db] = mfma_bf16_32x32x16(vf, pf[s2], oacc[db]);
                 }
             if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
