@@ -87,6 +87,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
     float m = -INFINITY;  // reference maximum of the scaled (log2-domain) scores
+    float mneg = 0.f;     // -m, or 0 while m = -inf (a row with nothing visible yet)
     float l = 0.f;        // running partial sum over this lane's keys
 
     int ntiles = (N + BC - 1) / BC;
@@ -181,8 +182,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
                 m = m_new;
+                mneg = (m == -INFINITY) ? 0.f : -m;
             }
-            const float m_use = (m == -INFINITY) ? 0.f : m;  // row with nothing visible yet
             float rs0 = 0.f, rs1 = 0.f;
             bf16x8 pf[BC / 16];
             u32x4 dw[2];
@@ -194,9 +195,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float p = fast_exp2(fmaf(s[kb][i], scale_log2, -m_use));
-                    if (i & 1) rs1 += p;
-                    else rs0 += p;
+                    const float p = fast_exp2(fmaf(s[kb][i], scale_log2, mneg));
+                    // The two sums start from the first two values (p >= 0, so 0 + p = p).
+                    if (kb == 0 && i < 2) (i ? rs1 : rs0) = p;
+                    else (i & 1 ? rs1 : rs0) += p;
                     float pv = p;
                     if constexpr (DROPOUT) pv = dropout_keep(dw[kb], i, dp.thr) ? p : 0.f;
                     // k-step s2 = 2 kb + i/8 covers keys 16 s2 + 8 (j/4) + 4 h + j%4, j = i%8
