@@ -84,8 +84,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_preprocess_kernel(const bf16*
                                                                      float* __restrict__ Dl, int64_t rows) {
     constexpr int DCH = D / 8;
     constexpr int ROWS_PER_BLOCK = kBwdThreads / DCH;
-    const int tid = threadIdx.x;
-    const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + tid / DCH;
+    const int tid = thread_id();
+    const int64_t row = (int64_t)block_id() * ROWS_PER_BLOCK + tid / DCH;
     const int ch = tid % DCH;
     float acc = 0.f;
     if (row < rows) {
@@ -145,14 +145,14 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(16))) float sD[2][BQ];
     __shared__ __attribute__((aligned(16))) uint32_t sKeep[DROPOUT ? kBwdWaves : 1][32];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int tid = thread_id(), lane = tid & 63, w = wave_id();
     const int lq = lane & 31, h = lane >> 5;
     // Flat id -> (key/value head, key block): XCD-contiguous, head-major; key
     // blocks ascend, so for causal masks the heaviest blocks (the first ones,
     // seen by the most queries) start first.  The G query heads sharing the
     // key/value head (grouped heads) are walked one after the other, their
     // contributions summed in the same accumulators.
-    const int task = xcd_task(blockIdx.x, BKV * nkb);
+    const int task = xcd_task(block_id(), BKV * nkb);
     if (task >= BKV * nkb) return;
     const int kvh = task / nkb;
     const int kb = task % nkb;
@@ -370,9 +370,9 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
     __shared__ __attribute__((aligned(16))) bf16 sK[2][BKV * KS];
     __shared__ __attribute__((aligned(16))) bf16 sV[2][BKV * VS];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int tid = thread_id(), lane = tid & 63, w = wave_id();
     const int lq = lane & 31, h = lane >> 5;
-    const int task = xcd_task(blockIdx.x, BH * nqb);
+    const int task = xcd_task(block_id(), BH * nqb);
     if (task >= BH * nqb) return;
     const int bh = task / nqb;
     const int qi = task % nqb;

@@ -147,8 +147,10 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        // Full 64-bit products (one v_mad_u64_u32 each) give both halves.
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
         c0 = hi1 ^ c1 ^ k0;
         c1 = lo1;
         c2 = hi0 ^ c3 ^ k1;
@@ -196,9 +198,16 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
                                             __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)});
 }
 
+// Work-item and workgroup ids read straight from the hardware registers.  The
+// threadIdx / blockIdx accessors go through device-library functions built with
+// other target features than these kernels (packed fp32 is disabled here), so
+// the compiler calls them instead of inlining them; so would __umulhi.
+__device__ __forceinline__ int thread_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int block_id() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+
 // Index of the calling wavefront in its workgroup, as a scalar (wave-uniform)
 // value so that branches on it are scalar branches.
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(thread_id() >> 6); }
 
 // Maximum of the 32 score registers of two 32x32 C tiles (v_max3_f32 chains).
 __device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {

@@ -65,9 +65,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
     __shared__ float sM[kDecWaves][kDecSlots], sL[kDecWaves][kDecSlots];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int tid = thread_id(), lane = tid & 63, w = wave_id();
     const int lq = lane & 31, h = lane >> 5;
-    const int task = xcd_task(blockIdx.x, tasks);
+    const int task = xcd_task(block_id(), tasks);
     if (task >= tasks) return;
     // Task order: (batch, key/value head), split, query group -- the query
     // groups of one split are neighbours and share its K/V in one XCD's L2.
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
                                                            float* __restrict__ LSE, int BHq, int splits) {
     constexpr int PER = D / 64;
     constexpr int AHEAD = 16;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int row = block_id() * 4 + (thread_id() >> 6), lane = thread_id() & 63;
     if (row >= BHq) return;
     float mstar = -INFINITY;
     for (int s = lane; s < splits; s += 64) mstar = fmaxf(mstar, part_ml[2 * ((int64_t)s * BHq + row)]);

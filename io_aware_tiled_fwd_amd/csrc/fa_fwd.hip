@@ -61,10 +61,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     __shared__ __attribute__((aligned(16))) bf16 sK[2][BC * KS];
     __shared__ __attribute__((aligned(16))) bf16 sV[2][BC * VS];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int tid = thread_id(), lane = tid & 63, w = wave_id();
     const int lq = lane & 31, h = lane >> 5;
     int bh, qb;
-    if (!wg_coords(blockIdx.x, BH, nqb, CAUSAL, bh, qb)) return;
+    if (!wg_coords(block_id(), BH, nqb, CAUSAL, bh, qb)) return;
     const int q0 = qb * kFwdBr;
     const int qw0 = q0 + 32 * w;  // first query row of this wave
     const int qrow = qw0 + lq;    // this lane's query row
@@ -257,10 +257,10 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_f32_kernel(
     __shared__ __attribute__((aligned(16))) float sK[BC * KS];
     __shared__ __attribute__((aligned(16))) float sV[BC * VS];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = thread_id(), lane = tid & 63, w = tid >> 6;
     const int lq = lane & 31, h = lane >> 5;
     int bh, qb;
-    if (!wg_coords(blockIdx.x, BH, nqb, CAUSAL, bh, qb)) return;
+    if (!wg_coords(block_id(), BH, nqb, CAUSAL, bh, qb)) return;
     const int q0 = qb * kFwdBr;
     const int qw0 = q0 + 32 * w;
     const int qrow = qw0 + lq;

@@ -89,10 +89,10 @@ __global__ __launch_bounds__(kF8Threads, 1) void fwd_fp8_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t sK[2][BC * KS];
     __shared__ __attribute__((aligned(16))) uint8_t sVt[2][D * VTS];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int tid = thread_id(), lane = tid & 63, w = wave_id();
     const int lq = lane & 31, h = lane >> 5;
     int bh, qb;
-    if (!wg_coords(blockIdx.x, BH, nqb, CAUSAL, bh, qb)) return;
+    if (!wg_coords(block_id(), BH, nqb, CAUSAL, bh, qb)) return;
     const int q0 = qb * kF8Br;
     const int qw0 = q0 + 32 * w;
     const int qrow = qw0 + lq;
