@@ -236,8 +236,31 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
             if (!CAUSAL || __builtin_amdgcn_readfirstlane(i0 + BQ - 1 >= kw0)) {
                 const bf16* qt = sQ[buf];
                 const bf16* gt = sdO[buf];
+                // dV: the scores of every 32-query sub-block first, as
+                // interleaved accumulation chains (one chain alone would wait
+                // on each previous MFMA).  It has registers to spare: each Q
+                // fragment is requested AHEAD MFMAs before its use (volatile
+                // reads keep that order).
+                constexpr int NQH = BQ / 32;
+                f32x16 sv[DK ? 1 : NQH];
+                if constexpr (!DK) {
+                    constexpr int NR = NQH * (D / 16), AHEAD = 4;
+                    auto qread = [&](int r) {
+                        return lds_read16_early(qt + 32 * (r % NQH) * RS + row_off + 16 * (r / NQH));
+                    };
+                    bf16x8 qa[NR];
 #pragma unroll
-                for (int qh = 0; qh < BQ / 32; ++qh) {
+                    for (int r = 0; r < AHEAD; ++r) qa[r] = qread(r);
+#pragma unroll
+                    for (int qh = 0; qh < NQH; ++qh) sv[qh] = f32x16{};
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) {
+                        if (r + AHEAD < NR) qa[r + AHEAD] = qread(r + AHEAD);
+                        sv[r % NQH] = mfma_bf16_32x32x16(qa[r], kf[r / NQH], sv[r % NQH]);
+                    }
+                }
+#pragma unroll
+                for (int qh = 0; qh < NQH; ++qh) {
                     // (The keep bits are formed before the score MFMAs, while
                     // fewer accumulators are live.)
                     uint32_t keep_bits[4];  // bit lq of word e of group r: query 32 qh + 8 r + 4 h + e kept
@@ -268,19 +291,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
                             dp = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(gt + off), vf[ks], dp);
                         }
                     } else {
-                        // dV has registers to spare: each Q fragment is requested four
-                        // MFMAs before its use (volatile reads keep that order).
-                        constexpr int AHEAD = 4;
-                        bf16x8 qa[D / 16];
-#pragma unroll
-                        for (int ks = 0; ks < AHEAD; ++ks)
-                            qa[ks] = lds_read16_early(qt + 32 * qh * RS + row_off + 16 * ks);
-#pragma unroll
-                        for (int ks = 0; ks < D / 16; ++ks) {
-                            if (ks + AHEAD < D / 16)
-                                qa[ks + AHEAD] = lds_read16_early(qt + 32 * qh * RS + row_off + 16 * (ks + AHEAD));
-                            s = mfma_bf16_32x32x16(qa[ks], kf[ks], s);
-                        }
+                        s = sv[qh];
                     }
                     // Register i holds query 32 qh + c_row(i, h); four consecutive queries per float4.
                     float v[16];
