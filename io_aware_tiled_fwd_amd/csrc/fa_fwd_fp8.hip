@@ -116,6 +116,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void fwd_fp8_kernel(
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
     float m = -INFINITY, l = 0.f;
+    float mneg = 0.f;  // -m, or 0 while m = -inf (a row with nothing visible yet)
 
     int ntiles = (N + BC - 1) / BC;
     if (CAUSAL) ntiles = min(ntiles, (min(q0 + kF8Br, N) - 1) / BC + 1);
@@ -199,17 +200,18 @@ __global__ __launch_bounds__(kF8Threads, 1) void fwd_fp8_kernel(
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
                 m = m_new;
+                mneg = (m == -INFINITY) ? 0.f : -m;
             }
-            const float m_use = (m == -INFINITY) ? 0.f : m;
             float p[2][16];
             float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    p[kb][i] = fast_exp2(fmaf(s[kb][i], scale_log2, -m_use));
-                    if (i & 1) rs1 += p[kb][i];
-                    else rs0 += p[kb][i];
+                    p[kb][i] = fast_exp2(fmaf(s[kb][i], scale_log2, mneg));
+                    // The two sums start from the first two values (p >= 0, so 0 + p = p).
+                    if (kb == 0 && i < 2) (i ? rs1 : rs0) = p[kb][i];
+                    else (i & 1 ? rs1 : rs0) += p[kb][i];
                 }
             l += rs0 + rs1;
             // P~^T operand: byte 16 kb + i = e4m3(P of register i of block kb).
