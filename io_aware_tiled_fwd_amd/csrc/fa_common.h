@@ -186,6 +186,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, __builtin_amdgcn_readfirstlane(soff), 0);
 }
+// The same load with the non-temporal hint (cache policy nt), for data read
+// exactly once: a streaming read of 1 GiB measured 6.9-7.3 TB/s with it and
+// 5.6-6.5 TB/s without it on gfx950.
+__device__ __forceinline__ u32x4 buffer_load16_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, __builtin_amdgcn_readfirstlane(soff), 2);
+}
 
 // Round eight floats to bf16 (RNE) as four v_cvt_pk_bf16_f32.
 __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5,

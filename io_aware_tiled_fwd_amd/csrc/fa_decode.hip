@@ -53,7 +53,10 @@ struct DecLayout {
     static constexpr int CH = kDecTile * DCH / 64;     // chunks per lane per tile (K and V each)
 };
 
-template <int D>
+// STREAM: every K/V byte of the split is read by this workgroup only (one
+// query group), so the loads carry the non-temporal hint; with several query
+// groups the neighbouring workgroups re-read the split from L2.
+template <int D, bool STREAM>
 __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const int* __restrict__ kv_len, float* __restrict__ part_acc, float* __restrict__ part_ml,
@@ -109,8 +112,13 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
 #pragma unroll
         for (int r = 0; r < L::CH; ++r) {
             const int voff = ((ld_row + r * ROWS_PER_PASS) * D + 8 * ld_col) * 2;
-            kreg[r] = buffer_load16(krs, voff, soff);
-            vreg[r] = buffer_load16(vrs, voff, soff);
+            if constexpr (STREAM) {
+                kreg[r] = buffer_load16_nt(krs, voff, soff);
+                vreg[r] = buffer_load16_nt(vrs, voff, soff);
+            } else {
+                kreg[r] = buffer_load16(krs, voff, soff);
+                vreg[r] = buffer_load16(vrs, voff, soff);
+            }
         }
     };
     auto store_tile = [&]() {
@@ -337,8 +345,14 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const int*
     const dim3 grid(grid_for_tasks(tasks)), mgrid((BHq + 3) / 4);
 #define FA_DEC_LAUNCH(DD)                                                                                       \
     do {                                                                                                        \
-        hipLaunchKernelGGL((decode_split_kernel<DD>), grid, dim3(kDecThreads), 0, stream, Qp, Kp, Vp, kv_len, pacc, \
-                           pml, Op, lse, Hq, Hkv, Nk, plan.nqg, plan.splits, plan.chunk, tasks, BHq, sl2);      \
+        if (plan.nqg == 1)                                                                                      \
+            hipLaunchKernelGGL((decode_split_kernel<DD, true>), grid, dim3(kDecThreads), 0, stream, Qp, Kp, Vp,  \
+                               kv_len, pacc, pml, Op, lse, Hq, Hkv, Nk, plan.nqg, plan.splits, plan.chunk, tasks, \
+                               BHq, sl2);                                                                       \
+        else                                                                                                    \
+            hipLaunchKernelGGL((decode_split_kernel<DD, false>), grid, dim3(kDecThreads), 0, stream, Qp, Kp, Vp, \
+                               kv_len, pacc, pml, Op, lse, Hq, Hkv, Nk, plan.nqg, plan.splits, plan.chunk, tasks, \
+                               BHq, sl2);                                                                       \
         hipError_t e = hipGetLastError();                                                                       \
         if (e != hipSuccess || plan.splits == 1) return e;                                                      \
         hipLaunchKernelGGL((decode_merge_kernel<DD>), mgrid, dim3(256), 0, stream, pacc, pml, Op, lse, BHq,     \
