@@ -1,0 +1,87 @@
+"""Code-generation checks on the built library (CPU only: reads the gfx950 code
+objects inside libfa.so with the ROCm LLVM tools, runs nothing on a GPU).
+
+* No kernel makes a function call.  The kernels are built without packed-fp32
+  instructions and with IEEE mode off, so ROCm device-library functions
+  (threadIdx / blockIdx accessors, __umulhi, ...) are not inlined into them and
+  each use becomes an s_swappc_b64 call; the kernels read hardware registers and
+  use builtins instead, and this test keeps it that way.
+* The kernels of the measured paths spill no registers.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "io_aware_tiled_fwd_amd", "libfa.so")
+LLVM = "/opt/rocm/llvm/bin"
+TOOLS = {t: os.path.join(LLVM, t) for t in ("llvm-objcopy", "llvm-objdump", "llvm-readelf", "clang-offload-bundler")}
+TARGET = "hipv4-amdgcn-amd-amdhsa--gfx950"
+MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
+
+# Kernels (mangled-name fragments) that must not spill: the bf16 forward, the
+# backward stages and the decode, as the benchmark and the GPU tests run them.
+NO_SPILL = [
+    "fwd_bf16_kernelILi128ELb1ELb0E", "fwd_bf16_kernelILi128ELb0ELb0E",
+    "fwd_bf16_kernelILi64ELb1ELb0E", "fwd_bf16_kernelILi64ELb0ELb0E",
+    "fwd_bf16_kernelILi128ELb1ELb1E",
+    "bwd_dkdv_kernelILi128ELb1ELb1ELb0ELb0EfE", "bwd_dkdv_kernelILi128ELb1ELb0ELb0ELb0EfE",
+    "bwd_dq_kernelILi128ELb1ELb0EfE", "bwd_preprocess_kernelILi128E",
+    "fwd_fp8_kernelILi128ELb1E", "decode_split_kernelILi128ELb1E", "decode_merge_kernelILi128E",
+]
+
+
+@pytest.fixture(scope="module")
+def code_objects(tmp_path_factory):
+    if not os.path.exists(LIB):
+        pytest.skip("libfa.so is not built")
+    if not all(os.path.exists(p) for p in TOOLS.values()):
+        pytest.skip("ROCm LLVM tools not found")
+    tmp = tmp_path_factory.mktemp("co")
+    fatbin = tmp / "fatbin.bin"
+    subprocess.run([TOOLS["llvm-objcopy"], f"--dump-section=.hip_fatbin={fatbin}", LIB, os.devnull], check=True)
+    data = fatbin.read_bytes()
+    starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)]
+    assert starts, "no offload bundle in .hip_fatbin"
+    objs = []
+    for n, (a, b) in enumerate(zip(starts, starts[1:] + [len(data)])):
+        chunk = tmp / f"bundle{n}.bin"
+        chunk.write_bytes(data[a:b])
+        co = tmp / f"code{n}.co"
+        r = subprocess.run([TOOLS["clang-offload-bundler"], "--unbundle", "--type=o", f"--targets={TARGET}",
+                            f"--input={chunk}", f"--output={co}"], capture_output=True)
+        if r.returncode == 0 and co.exists() and co.stat().st_size > 0:
+            objs.append(co)
+    assert objs, "no gfx950 code object found"
+    return objs
+
+
+def test_no_function_calls(code_objects):
+    for co in code_objects:
+        dis = subprocess.run([TOOLS["llvm-objdump"], "-d", str(co)], capture_output=True, text=True, check=True).stdout
+        assert "v_mfma" in dis or "s_endpgm" in dis, "disassembly looks empty"
+        calls = dis.count("s_swappc_b64")
+        assert calls == 0, f"{co.name}: {calls} function calls (s_swappc_b64) in the kernels"
+
+
+def test_hot_kernels_do_not_spill(code_objects):
+    spills = {}
+    for co in code_objects:
+        notes = subprocess.run([TOOLS["llvm-readelf"], "--notes", str(co)], capture_output=True, text=True,
+                               check=True).stdout
+        name = None
+        for line in notes.splitlines():
+            m = re.match(r"\s+\.name:\s+(\S+)", line)
+            if m:
+                name = m.group(1)
+            m = re.match(r"\s+\.vgpr_spill_count:\s+(\d+)", line)
+            if m and name:
+                spills[name] = int(m.group(1))
+    for frag in NO_SPILL:
+        hits = {n: c for n, c in spills.items() if frag in n}
+        assert hits, f"kernel {frag} not found in the code objects"
+        for n, c in hits.items():
+            assert c == 0, f"{n} spills {c} VGPRs"
