@@ -234,6 +234,42 @@ def decode_leg(name, iters=50, warmup=5):
                          "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def probe_leg(mfma_blocks=1024, mfma_iters=2000, read_mib=1024, reps=3):
+    """Measured ceilings beside the published peaks: the library's bf16 MFMA
+    loop and its non-temporal HBM read sweep (include/fa_probe.h), timed with
+    HIP events on the launch stream (best of `reps` after one warm-up).  The
+    roofline fractions above stay against the published peaks."""
+    import torch
+
+    from io_aware_tiled_fwd_amd import binding
+
+    stream = torch.cuda.current_stream()
+
+    def best_ms(call):
+        call()
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    sink = torch.empty(mfma_blocks * 512, dtype=torch.float32, device="cuda")
+    ms = best_ms(lambda: binding.fa_probe_mfma(mfma_blocks, mfma_iters, sink, stream))
+    tflops = mfma_blocks * 8 * mfma_iters * 16 * 32768 / (ms / 1e3) / 1e12
+    nbytes = read_mib * 2**20 // binding.PROBE_READ_UNIT * binding.PROBE_READ_UNIT
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    rsink = torch.empty(256 * 512, dtype=torch.int32, device="cuda")
+    ms_r = best_ms(lambda: binding.fa_probe_hbm_read(buf, rsink, stream))
+    del buf
+    return {"mfma_bf16_tflops": round(tflops, 1), "hbm_read_gbs": round(nbytes / (ms_r / 1e3) / 1e9, 1),
+            "how": f"{mfma_blocks} workgroups x 8 waves of v_mfma_f32_32x32x16_bf16 on four chains; "
+                   f"{nbytes >> 20} MiB read once with 16-byte non-temporal loads (fa_probe.h)"}
+
+
 def cpu_baseline(heads, causal):
     """The fp64 oracle, as it stands, on host cores: forward + backward of the
     first few heads of the benchmark's own inputs (batch 0), each over all N
@@ -271,6 +307,7 @@ def main(argv=None):
                     help="split-KV decode workload timed after the training step ('none' to skip)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward leg")
     ap.add_argument("--no-dropout", action="store_true", help="skip the dropout fwd+bwd leg")
+    ap.add_argument("--no-probe", action="store_true", help="skip the measured MFMA / HBM-read ceilings")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of batch 0 the CPU baseline computes (about 10-20 s)")
     args = ap.parse_args(argv)
@@ -391,6 +428,8 @@ def main(argv=None):
     del t
     if args.decode != "none":
         out["decode"] = decode_leg(args.decode)
+    if not args.no_probe:
+        out["measured_ceilings"] = probe_leg()
     if not args.no_cpu_baseline:
         cb = cpu_baseline(cpu_heads, causal)
         out["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cb.items()

@@ -24,7 +24,7 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_fwd_gqa", "fa_bwd_gqa", "fa_bwd_gqa_bf16grad",
            "fa_fwd_dropout",
            "fa_bwd_dropout", "fa_decode_plan", "fa_decode", "fa_bwd_preprocess", "fa_bwd_dv", "fa_bwd_dk",
-           "fa_bwd_dq", "fa_status_string")
+           "fa_bwd_dq", "fa_status_string", "fa_probe_mfma", "fa_probe_hbm_read")
 
 
 class FaError(RuntimeError):
@@ -63,9 +63,12 @@ def load_library():
     lib.fa_bwd_dv.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dk.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dq.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
+    lib.fa_probe_mfma.argtypes = [i, i, vp, vp]
+    lib.fa_probe_hbm_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
     for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_fwd_fp8, lib.fa_fwd_dropout, lib.fa_bwd_dropout,
                lib.fa_bwd_gqa_bf16grad, lib.fa_bwd, lib.fa_fwd_gqa, lib.fa_bwd_gqa, lib.fa_decode_plan,
-               lib.fa_decode, lib.fa_bwd_preprocess, lib.fa_bwd_dv, lib.fa_bwd_dk, lib.fa_bwd_dq):
+               lib.fa_decode, lib.fa_bwd_preprocess, lib.fa_bwd_dv, lib.fa_bwd_dk, lib.fa_bwd_dq,
+               lib.fa_probe_mfma, lib.fa_probe_hbm_read):
         fn.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -514,3 +517,28 @@ def fa_bwd_gqa_bf16grad(q, k, v, o, lse, dout, dq, dk, dv, delta, causal=False, 
                                             ctypes.c_void_p(_stream_handle(stream)))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_gqa_bf16grad")
+
+
+# Measurement probes (include/fa_probe.h): not part of the attention method.
+PROBE_READ_UNIT = 16 * 512 * 256 * 4  # fa_probe_hbm_read sizes are multiples of this (8 MiB)
+
+
+def fa_probe_mfma(blocks, iters, sink, stream=None) -> None:
+    """bf16 MFMA throughput loop: blocks * 8 * iters * 16 * 32768 FLOP; sink
+    fp32 [blocks * 512] on the GPU (written, values meaningless)."""
+    if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() < blocks * 512:
+        raise ValueError("sink must be a CUDA float32 tensor of at least blocks * 512 elements")
+    st = load_library().fa_probe_mfma(blocks, iters, _ptr(sink), _stream_handle(stream))
+    if st:
+        raise FaError(st, "fa_probe_mfma")
+
+
+def fa_probe_hbm_read(buf, sink, stream=None) -> None:
+    """Non-temporal read sweep over the bytes of buf (a multiple of
+    PROBE_READ_UNIT); sink int32 [256 * 512] on the GPU."""
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_cuda or not sink.is_cuda or sink.numel() < 256 * 512 or sink.element_size() != 4:
+        raise ValueError("buf and sink must be CUDA tensors; sink of at least 256 * 512 4-byte elements")
+    st = load_library().fa_probe_hbm_read(_ptr(buf), nbytes, _ptr(sink), _stream_handle(stream))
+    if st:
+        raise FaError(st, "fa_probe_hbm_read")

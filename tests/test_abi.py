@@ -252,3 +252,17 @@ def test_oracle_and_gpu_path_share_no_code():
         if f.endswith((".py", ".c", ".h")):
             text = open(os.path.join(ROOT, "oracle", f)).read()
             assert "io_aware_tiled_fwd_amd" not in text and "fa_common" not in text, f
+
+
+def test_probe_rejections(lib):
+    """The measurement probes check their arguments before any launch."""
+    FA_ERR_INVALID_ARG = 1
+    sink = FAKE
+    assert lib.fa_probe_mfma(0, 10, sink, None) == FA_ERR_INVALID_ARG
+    assert lib.fa_probe_mfma(4, 0, sink, None) == FA_ERR_INVALID_ARG
+    assert lib.fa_probe_mfma(4, 10, None, None) == FA_ERR_INVALID_ARG
+    unit = 16 * 512 * 256 * 4
+    assert lib.fa_probe_hbm_read(sink, unit + 16, sink, None) == FA_ERR_INVALID_ARG
+    assert lib.fa_probe_hbm_read(sink, 0, sink, None) == FA_ERR_INVALID_ARG
+    assert lib.fa_probe_hbm_read(None, unit, sink, None) == FA_ERR_INVALID_ARG
+    assert lib.fa_probe_hbm_read(ctypes.c_void_p(0x1008), unit, sink, None) == FA_ERR_INVALID_ARG
