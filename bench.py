@@ -386,6 +386,8 @@ def main(argv=None):
     kflops = kernel_flops(B, H, N, d, causal)
     kbytes = kernel_bytes(B, H, N, d)
     kernels = {n: {"ms_median": round(med[n], 4), "ms_mean": round(avg[n], 4),
+                   "ms_p10": round(float(np.percentile(per[n], 10)), 4),
+                   "ms_p90": round(float(np.percentile(per[n], 90)), 4),
                    "tflops": round(kflops[n] / (avg[n] / 1e3) / 1e12, 2),
                    "gbs_compulsory": round(kbytes[n] / (avg[n] / 1e3) / 1e9, 1)} for n in names}
     dominant = max(("fwd", "bwd_dv", "bwd_dk", "bwd_dq"), key=lambda n: avg[n])
