@@ -143,10 +143,12 @@ def fp8_leg(t, B, H, N, d, causal, scale, iters=20, warmup=3):
         call()
         e1.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    times = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms = float(np.median(times))  # the median resists a transient slow period of the box
     ff, _ = counted_flops(B, H, N, d, causal)
     tf = ff / (ms / 1e3) / 1e12
-    return {"ms_mean": round(ms, 4), "tflops": round(tf, 2), "frac_peak_fp8": round(tf / PEAK_FP8_TFLOPS, 4),
+    return {"ms_median": round(ms, 4), "ms_mean": round(float(np.mean(times)), 4), "tflops": round(tf, 2),
+            "frac_peak_fp8": round(tf / PEAK_FP8_TFLOPS, 4),
             "inputs": "the step's Q, K, V quantised on the device to e4m3, one factor per tensor"}
 
 
@@ -185,8 +187,9 @@ def dropout_leg(t, B, H, N, d, causal, scale, p=0.1, iters=10, warmup=2):
         bwd()
         e[2].record(stream)
     torch.cuda.synchronize()
-    fms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    bms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    # medians: they resist a transient slow period of the box
+    fms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    bms = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
     ff, fb = counted_flops(B, H, N, d, causal)
     return {"p": p, "fwd_ms": round(fms, 4), "bwd_ms": round(bms, 4),
             "fwd_tflops": round(ff / (fms / 1e3) / 1e12, 2), "bwd_tflops": round(fb / (bms / 1e3) / 1e12, 2)}
@@ -224,11 +227,11 @@ def decode_leg(name, iters=50, warmup=5):
         e1.record(stream)
     torch.cuda.synchronize()
     ms = [e0.elapsed_time(e1) for e0, e1 in ev]
-    mean_us = float(np.mean(ms)) * 1e3
+    med_us = float(np.median(ms)) * 1e3  # the median resists a transient slow period of the box
     nbytes = 2 * B * Hkv * Nk * d * 2 + 2 * B * Hq * d * 2 + 4 * B * Hq
-    gbs = nbytes / (mean_us / 1e6) / 1e9
+    gbs = nbytes / (med_us / 1e6) / 1e9
     return {"workload": name, "B": B, "Hq": Hq, "Hkv": Hkv, "Nk": Nk, "d": d, "splits": splits,
-            "us_mean": round(mean_us, 2), "us_median": round(float(np.median(ms)) * 1e3, 2),
+            "us_median": round(med_us, 2), "us_mean": round(float(np.mean(ms)) * 1e3, 2),
             "bytes_compulsory": nbytes,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4)}}
