@@ -208,10 +208,14 @@ int fa_decode(const void* q, const void* k, const void* v, const int* kv_len, vo
               size_t workspace_bytes, hipStream_t stream);
 
 /*
- * The four stages of fa_bwd, for callers that schedule or time them
- * separately.  Calling them in this order on one stream is exactly fa_bwd.
+ * The stages of fa_bwd, for callers that schedule or time them separately.
+ * fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq in this order on one stream are
+ * exactly fa_bwd (the kernels fa_bwd runs).  fa_bwd_dv and fa_bwd_dk compute
+ * the same dV and dK as fa_bwd_dkdv, bitwise, with one kernel each (S is then
+ * computed twice).
  *
  * fa_bwd_preprocess: delta[i] = sum_t dO_it * O_it (fp32), o and dO bf16.
+ * fa_bwd_dkdv:       dK and dV (fp32) from q, k, v, dO (bf16), lse and delta.
  * fa_bwd_dv:         dV (fp32) from q, k, dO (bf16) and lse.
  * fa_bwd_dk:         dK (fp32) from q, k, v, dO (bf16), lse and delta.
  * fa_bwd_dq:         dQ (fp32) from q, k, v, dO (bf16), lse and delta.
@@ -219,6 +223,9 @@ int fa_decode(const void* q, const void* k, const void* v, const int* kv_len, vo
  */
 int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H, int N, int d,
                       hipStream_t stream);
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+                const float* delta, float* dk, float* dv, int B, int H, int N, int d, float scale,
+                int causal, hipStream_t stream);
 int fa_bwd_dv(const void* q, const void* k, const float* lse, const void* dO, float* dv,
               int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 int fa_bwd_dk(const void* q, const void* k, const void* v, const float* lse, const void* dO,

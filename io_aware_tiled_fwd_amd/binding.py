@@ -23,8 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_fwd_gqa", "fa_bwd_gqa", "fa_bwd_gqa_bf16grad",
            "fa_fwd_dropout",
-           "fa_bwd_dropout", "fa_decode_plan", "fa_decode", "fa_bwd_preprocess", "fa_bwd_dv", "fa_bwd_dk",
-           "fa_bwd_dq", "fa_status_string", "fa_probe_mfma", "fa_probe_hbm_read")
+           "fa_bwd_dropout", "fa_decode_plan", "fa_decode", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dv",
+           "fa_bwd_dk", "fa_bwd_dq", "fa_status_string", "fa_probe_mfma", "fa_probe_hbm_read")
 
 
 class FaError(RuntimeError):
@@ -62,12 +62,13 @@ def load_library():
     lib.fa_bwd_preprocess.argtypes = [vp] * 3 + [i, i, i, i, vp]
     lib.fa_bwd_dv.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dk.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
+    lib.fa_bwd_dkdv.argtypes = [vp] * 8 + [i, i, i, i, f, i, vp]
     lib.fa_bwd_dq.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp]
     lib.fa_probe_mfma.argtypes = [i, i, vp, vp]
     lib.fa_probe_hbm_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
     for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_fwd_fp8, lib.fa_fwd_dropout, lib.fa_bwd_dropout,
                lib.fa_bwd_gqa_bf16grad, lib.fa_bwd, lib.fa_fwd_gqa, lib.fa_bwd_gqa, lib.fa_decode_plan,
-               lib.fa_decode, lib.fa_bwd_preprocess, lib.fa_bwd_dv, lib.fa_bwd_dk, lib.fa_bwd_dq,
+               lib.fa_decode, lib.fa_bwd_preprocess, lib.fa_bwd_dkdv, lib.fa_bwd_dv, lib.fa_bwd_dk, lib.fa_bwd_dq,
                lib.fa_probe_mfma, lib.fa_probe_hbm_read):
         fn.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [i]
@@ -283,6 +284,17 @@ def fa_bwd_dk(q, k, v, lse, dout, delta, dk, causal=False, scale=None, stream=No
                                   ctypes.c_void_p(_stream_handle(stream)))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_dk")
+
+
+def fa_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, causal=False, scale=None, stream=None) -> None:
+    """dK and dV (fp32) given lse and delta, in one stage."""
+    B, H, N, d = _check_bwd_args(q, k, v, dout, lse, delta, ((dk, "dk"), (dv, "dv")))
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta),
+                                    _ptr(dk), _ptr(dv), B, H, N, d, sc, int(bool(causal)),
+                                    ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dkdv")
 
 
 def fa_bwd_dq(q, k, v, lse, dout, delta, dq, causal=False, scale=None, stream=None) -> None:

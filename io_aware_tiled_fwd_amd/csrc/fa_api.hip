@@ -209,6 +209,18 @@ int fa_bwd_dk(const void* q, const void* k, const void* v, const float* lse, con
         fa::launch_bwd_dk(q, k, v, lse, dO, delta, dk, B, H, H, N, d, scale, causal != 0, nullptr, false, stream));
 }
 
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dO, const float* delta,
+                float* dk, float* dv, int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
+    if (!q || !k || !v || !lse || !dO || !delta || !dk || !dv) return FA_ERR_INVALID_ARG;
+    const int st = check_shape(B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    const void* ptrs[] = {q, k, v, lse, dO, delta, dk, dv};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+    return from_hip(fa::launch_bwd_dkdv(q, k, v, lse, dO, delta, dk, dv, B, H, H, N, d, scale, causal != 0, nullptr,
+                                        false, stream));
+}
+
 int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO, const float* delta,
               float* dq, int B, int H, int N, int d, float scale, int causal, hipStream_t stream) {
     if (!q || !k || !v || !lse || !dO || !delta || !dq) return FA_ERR_INVALID_ARG;

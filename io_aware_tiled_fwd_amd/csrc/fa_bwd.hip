@@ -7,15 +7,18 @@
 // dK = scale dS^T Q and dQ = scale dS K.  Only the O(N) statistics L and D are
 // read besides the O(N d) tensors; no N x N matrix reaches HBM.
 //
-// Three kernels run in stream order:
+// Three stages run in stream order:
 //   1. preprocess   D_i = sum_t dO_it O_it                    (bandwidth-bound)
-//   2. dV, dK       two kernels, one workgroup per 128 keys (32 per
-//                   wavefront), walking the query blocks; the wavefront's K (and
-//                   V) rows stay in registers as MFMA operands, and dV (or dK)
-//                   accumulates in registers and is written once.  Splitting
-//                   them recomputes S once more but halves the accumulator
-//                   registers, so two wavefronts share each SIMD.
-//   3. dQ           one workgroup per 128 query rows (32 per wavefront),
+//   2. dK, dV       at d = 128 one kernel of paired wavefronts (2'. below):
+//                   a workgroup per 128 keys, walking the query blocks; one
+//                   wavefront of a pair computes P and dV, hands P to its
+//                   partner through LDS, and the partner computes dS and dK.
+//                   At d = 64 two kernels (2. below), one workgroup per 256 keys
+//                   (32 per wavefront), each recomputing S.  The wavefront's K
+//                   (or V) rows stay in registers as MFMA operands, and its one
+//                   gradient accumulates in registers and is written once, so
+//                   two wavefronts share each SIMD.
+//   3. dQ           one workgroup per 256 query rows (32 per wavefront),
 //                   walking the key tiles; dQ accumulates in registers.
 // Tiles are staged row-major in double-buffered LDS through buffer loads (rows
 // past N read as zero); operands that must be transposed (dO^T, Q^T, K^T) are
@@ -355,6 +358,272 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// 2'. dK and dV in one kernel, by paired wavefronts (d = 128).  A workgroup
+//    owns 128 keys; wavefront pair p (wavefronts p and p + 4) owns keys
+//    32 p .. 32 p + 31.  The first of the pair computes S and P (as the dV
+//    kernel does), hands P to its partner through LDS and accumulates dV; the
+//    second computes dP and, with its partner's P, dS and dK.  S is thus
+//    computed once for both gradients (8 products per tile instead of the
+//    separate kernels' 10) while each wavefront still holds a single fp32
+//    accumulator, so two wavefronts share each SIMD as before.  Per 64-query
+//    step:
+//      phase 1  dV wavefront: S, P (masked), P -> LDS      dK wavefront: dP - D
+//      barrier
+//      phase 2  dV wavefront: dV^T += dO^T P              dK wavefront: dS, dK^T += Q^T dS
+//    P crosses in fp32 and every value is formed by the same operations in
+//    the same order as in the separate kernels, so the results are bitwise
+//    those of the dV and dK kernels.  With dropout the dV wavefront hands P
+//    with its sign bit set where the element is dropped; the dK wavefront
+//    needs no generator of its own.  (At d = 64 the separate kernels are
+//    faster and are used instead.)
+constexpr int kPairs = kBwdWaves / 2;
+constexpr int kFusedBkv = 32 * kPairs;  // keys per workgroup
+
+template <int D, bool CAUSAL, bool GROUPED, bool DROPOUT, typename OutT>
+__global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
+    OutT* __restrict__ dKout, OutT* __restrict__ dVout, int N, int BKV, int nkb, float scale_log2, float dk_scale,
+    float dv_scale, int Hq, int G_arg, DropoutParams drop) {
+    static_assert(D == 128, "the paired kernel is built for d = 128");
+    const int G = GROUPED ? G_arg : 1;
+    constexpr int BQ = kDkvBq;
+    constexpr int NQH = BQ / 32;
+    constexpr int RS = both_ways_stride<D>();
+    __shared__ __attribute__((aligned(16))) bf16 sQ[2][BQ * RS];
+    __shared__ __attribute__((aligned(16))) bf16 sdO[2][BQ * RS];
+    __shared__ __attribute__((aligned(16))) float sL[2][BQ];
+    __shared__ __attribute__((aligned(16))) float sD[2][BQ];
+    // P of pair p, sub-block qh, register group r, lane: one float4 per lane.
+    __shared__ __attribute__((aligned(16))) f32x4 sP[kPairs][NQH][4][64];
+    __shared__ __attribute__((aligned(16))) uint32_t sKeep[DROPOUT ? kPairs : 1][32];
+
+    const int tid = thread_id(), lane = tid & 63, w = wave_id();
+    const int lq = lane & 31, h = lane >> 5;
+    // Wavefronts w and w + 4 share a SIMD (measured: pairing w with w + 1
+    // instead is 7% slower), so each SIMD runs one wavefront of each role.
+    const bool dvw = w < kPairs;  // wave-uniform role
+    const int pr = dvw ? w : w - kPairs;
+    // Flat id -> (key/value head, key block) as in the separate kernels.
+    const int task = xcd_task(block_id(), BKV * nkb);
+    if (task >= BKV * nkb) return;
+    const int kvh = task / nkb;
+    const int kb = task % nkb;
+    const int k0 = kb * kFusedBkv;
+    const int kw0 = k0 + 32 * pr;
+    const int key = kw0 + lq;
+    const int64_t base = (int64_t)kvh * N * D;
+    const int qh0 = (kvh / (Hq / G)) * Hq + (kvh % (Hq / G)) * G;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+
+    // K^T (dV wavefront) or V^T (dK wavefront) operands of this lane's key.
+    bf16x8 kvf[D / 16];
+    {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc((dvw ? K : V) + base, head_bytes);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            kvf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rs, (lq * D + 16 * ks + 8 * h) * 2, kw0 * D * 2));
+    }
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+
+    const int nqblk = (N + BQ - 1) / BQ;
+    const int iq0 = CAUSAL ? k0 / BQ : 0;
+    const int iq_split = CAUSAL ? min(nqblk, (k0 + kFusedBkv - 1) / BQ + 1) : iq0;
+    TileStager<D, BQ> stq(tid, RS), stg(tid, RS);
+    float lreg = 0.f, dreg = 0.f;
+    const int row_off = lq * RS + 8 * h;
+    const int tr_off = tr_row(lane) * RS + tr_col(lane);
+
+    auto run_head = [&](int qh_idx) {
+        const int64_t qbase = (int64_t)qh_idx * N;
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + qbase * D, head_bytes);
+        const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + qbase * D, head_bytes);
+        const float* lse_h = LSE + qbase;
+        const float* d_h = Dl + qbase;
+        auto load_block = [&](int iq) {
+            const int i0 = iq * BQ;
+            stq.load(qrs, i0);
+            stg.load(grs, i0);
+            if (tid < BQ) {
+                const int r = min(i0 + tid, N - 1);
+                lreg = i0 + tid < N ? lse_h[r] * kLog2e : INFINITY;
+                dreg = i0 + tid < N ? d_h[r] : 0.f;
+            }
+        };
+        auto store_block = [&](int buf) {
+            stq.store(sQ[buf], RS);
+            stg.store(sdO[buf], RS);
+            if (tid < BQ) {
+                sL[buf][tid] = lreg;
+                sD[buf][tid] = dreg;
+            }
+        };
+        if (iq0 < nqblk) {
+            load_block(iq0);
+            store_block(0);
+        }
+        __syncthreads();
+        auto step = [&](int iq, auto mask_tag) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            const int buf = (iq - iq0) & 1;
+            load_block(min(iq + 1, nqblk - 1));
+            const int i0 = iq * BQ;
+            const bool active = !CAUSAL || __builtin_amdgcn_readfirstlane(i0 + BQ - 1 >= kw0);
+            const bf16* qt = sQ[buf];
+            const bf16* gt = sdO[buf];
+            // Phase 1: S (dV wavefront, rows of Q) or dP (dK wavefront, rows of
+            // dO) for every 32-query sub-block, as interleaved chains with each
+            // row fragment requested AHEAD MFMAs before its use.
+            f32x16 t[NQH];
+            bf16x8 bop[2 * NQH];
+            if (active) {
+                const bf16* src = dvw ? qt : gt;
+                constexpr int NR = NQH * (D / 16), AHEAD = 4;
+                auto rread = [&](int r) {
+                    return lds_read16_early(src + 32 * (r % NQH) * RS + row_off + 16 * (r / NQH));
+                };
+                bf16x8 ra[NR];
+#pragma unroll
+                for (int r = 0; r < AHEAD; ++r) ra[r] = rread(r);
+#pragma unroll
+                for (int qh = 0; qh < NQH; ++qh) t[qh] = f32x16{};
+                // The S chain at raised priority: the partner's dP chain fills
+                // the MFMA unit while this wavefront computes P.
+                if (dvw) __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    if (r + AHEAD < NR) ra[r + AHEAD] = rread(r + AHEAD);
+                    t[r % NQH] = mfma_bf16_32x32x16(ra[r], kvf[r / NQH], t[r % NQH]);
+                }
+                if (dvw) __builtin_amdgcn_s_setprio(0);
+                // The dK wavefront forms dP - D while its partner computes P,
+                // leaving one product per element for phase 2.
+                if constexpr (!DROPOUT) {
+                    if (!dvw) {
+#pragma unroll
+                        for (int qh = 0; qh < NQH; ++qh)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[buf][32 * qh + 8 * r + 4 * h]);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) t[qh][4 * r + e] -= d4[e];
+                            }
+                    }
+                }
+                if (dvw) {
+#pragma unroll
+                    for (int qh = 0; qh < NQH; ++qh) {
+                        uint32_t keep_bits[4];  // bit lq of word e of group r: query 32 qh + 8 r + 4 h + e kept
+                        if constexpr (DROPOUT) {
+                            const u32x4 wd = dropout_words(drop, qh_idx, i0 + 32 * qh + lq, kw0 / 32, h);
+                            uint32_t bits = 0;
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                bits |= (dropout_keep(wd, r, drop.thr) ? 1u : 0u) << (8 * (r >> 2) + 4 * h + (r & 3));
+                            const auto sw = __builtin_amdgcn_permlane32_swap(bits, bits, false, false);
+                            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                            if (h == 0) sKeep[pr][lq] = sw[0] | sw[1];
+                            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const u32x4 k4 = *reinterpret_cast<const u32x4*>(&sKeep[pr][8 * r + 4 * h]);
+                                keep_bits[r] = ((k4[0] >> lq) & 1u) | (((k4[1] >> lq) & 1u) << 1) |
+                                               (((k4[2] >> lq) & 1u) << 2) | (((k4[3] >> lq) & 1u) << 3);
+                            }
+                        }
+                        float v[16];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][32 * qh + 8 * r + 4 * h]);
+                            f32x4 hand;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int i = 4 * r + e;
+                                float p = fast_exp2(fmaf(t[qh][i], scale_log2, -l4[e]));
+                                if constexpr (MASK) {
+                                    if (key > i0 + 32 * qh + c_row(i, h)) p = 0.f;
+                                }
+                                if constexpr (DROPOUT) {
+                                    const bool kept = (keep_bits[r] >> e) & 1u;
+                                    v[i] = kept ? p : 0.f;  // the keep scale rides in dv_scale
+                                    hand[e] = kept ? p : -p;
+                                } else {
+                                    v[i] = p;
+                                    hand[e] = p;
+                                }
+                            }
+                            sP[pr][qh][r][lane] = hand;
+                        }
+                        bop[2 * qh] = pack_bf16x8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+                        bop[2 * qh + 1] = pack_bf16x8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
+                    }
+                }
+            }
+            __syncthreads();  // P of every pair is in LDS
+            // Phase 2: the gradient products.
+            if (active) {
+                const bf16* at = dvw ? gt : qt;
+                if (!dvw) {
+#pragma unroll
+                    for (int qh = 0; qh < NQH; ++qh) {
+                        float v[16];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const f32x4 got = sP[pr][qh][r][lane];
+                            if constexpr (DROPOUT) {
+                                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[buf][32 * qh + 8 * r + 4 * h]);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    const float p = fabsf(got[e]);
+                                    const bool kept = !__builtin_signbit(got[e]);
+                                    v[4 * r + e] = p * ((kept ? drop.keep_scale * t[qh][4 * r + e] : 0.f) - d4[e]);
+                                }
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) v[4 * r + e] = got[e] * t[qh][4 * r + e];
+                            }
+                        }
+                        bop[2 * qh] = pack_bf16x8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+                        bop[2 * qh + 1] = pack_bf16x8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
+                    }
+                }
+                // A = Q^T (dK) or dO^T (dV): transposing reads; k-step s2 of
+                // sub-block qh covers queries 32 qh + 16 s2 + {4h + e, 8 + 4h + e}.
+#pragma unroll
+                for (int qh = 0; qh < NQH; ++qh) {
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+                        acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(at + 32 * qh * RS + tr_off + 32 * db, RS),
+                                                     bop[2 * qh], acc[db]);
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+                        acc[db] = mfma_bf16_32x32x16(
+                            lds_read_tr_a(at + (32 * qh + 16) * RS + tr_off + 32 * db, RS), bop[2 * qh + 1], acc[db]);
+                }
+            }
+            store_block(buf ^ 1);
+            __syncthreads();
+        };
+        for (int iq = iq0; iq < iq_split; ++iq) step(iq, std::true_type{});
+        for (int iq = max(iq0, iq_split); iq < nqblk; ++iq) step(iq, std::false_type{});
+    };
+    for (int g = 0; g < G; ++g) run_head(qh0 + g);
+
+    if (key < N) {
+        OutT* op = (dvw ? dVout : dKout) + base + (int64_t)key * D + 4 * h;
+        const float os = dvw ? dv_scale : dk_scale;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                store_grad4(op + 32 * db + 8 * r, f32x4{acc[db][4 * r] * os, acc[db][4 * r + 1] * os,
+                                                        acc[db][4 * r + 2] * os, acc[db][4 * r + 3] * os});
+    }
+}
+
+// ---------------------------------------------------------------------------
 // 3. dQ.  Per tile of 64 keys, staged row-major in LDS (double buffered): K
 //    (read both as rows and transposed) and V (rows).
 //    Per wavefront (32 queries) and 32-key half, with C tiles [key x query]:
@@ -526,6 +795,36 @@ hipError_t launch_dkdv_d(const bf16* q, const bf16* k, const bf16* v, const floa
                            q, k, v, dout, lse, delta, out, N, BKV, nkb, scale * kLog2e, out_scale, Hq, Hq / Hkv, dp);
     return hipGetLastError();
 }
+template <int D, bool CAUSAL, bool DROPOUT, typename OutT>
+hipError_t launch_dkdv_fused_d(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
+                               const float* delta, OutT* dk, OutT* dv, int B, int Hq, int Hkv, int N, float scale,
+                               const DropoutParams& dp, hipStream_t stream) {
+    const int nkb = (N + kFusedBkv - 1) / kFusedBkv, BKV = B * Hkv;
+    const dim3 grid(grid_for_tasks(nkb * BKV));
+    const float dv_scale = DROPOUT ? dp.keep_scale : 1.0f;
+    if (Hq == Hkv)
+        hipLaunchKernelGGL((bwd_dkdv_fused_kernel<D, CAUSAL, false, DROPOUT, OutT>), grid, dim3(kBwdThreads), 0,
+                           stream, q, k, v, dout, lse, delta, dk, dv, N, BKV, nkb, scale * kLog2e, scale, dv_scale,
+                           Hq, 1, dp);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_fused_kernel<D, CAUSAL, true, DROPOUT, OutT>), grid, dim3(kBwdThreads), 0,
+                           stream, q, k, v, dout, lse, delta, dk, dv, N, BKV, nkb, scale * kLog2e, scale, dv_scale,
+                           Hq, Hq / Hkv, dp);
+    return hipGetLastError();
+}
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv_fused_t(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
+                               const float* delta, void* dk, void* dv, int B, int Hq, int Hkv, int N, float scale,
+                               const DropoutParams* dropout, bool grad_bf16, hipStream_t stream) {
+    if (grad_bf16)
+        return launch_dkdv_fused_d<D, CAUSAL, false>(q, k, v, lse, dout, delta, static_cast<bf16*>(dk),
+                                                     static_cast<bf16*>(dv), B, Hq, Hkv, N, scale, kNoDropout, stream);
+    if (dropout)
+        return launch_dkdv_fused_d<D, CAUSAL, true>(q, k, v, lse, dout, delta, static_cast<float*>(dk),
+                                                    static_cast<float*>(dv), B, Hq, Hkv, N, scale, *dropout, stream);
+    return launch_dkdv_fused_d<D, CAUSAL, false>(q, k, v, lse, dout, delta, static_cast<float*>(dk),
+                                                 static_cast<float*>(dv), B, Hq, Hkv, N, scale, kNoDropout, stream);
+}
 // out: fp32, or bf16 when grad_bf16 (bf16 gradients have no dropout variant).
 template <int D, bool CAUSAL, bool DK>
 hipError_t launch_dkdv_t(const bf16* q, const bf16* k, const bf16* v, const float* lse, const bf16* dout,
@@ -598,6 +897,27 @@ hipError_t launch_bwd_dk(const void* q, const void* k, const void* v, const floa
 #undef FA_DK
 }
 
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                           const float* delta, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, float scale,
+                           bool causal, const DropoutParams* dropout, bool grad_bf16, hipStream_t stream) {
+    auto Q = static_cast<const bf16*>(q);
+    auto K = static_cast<const bf16*>(k);
+    auto V = static_cast<const bf16*>(v);
+    auto G = static_cast<const bf16*>(dout);
+    if (d == 64) {
+        // At d = 64 the separate kernels are faster: their steps are too short
+        // for the paired kernel's hand-over to pay.
+        hipError_t e = launch_bwd_dv(q, k, lse, dout, dv, B, Hq, Hkv, N, d, scale, causal, dropout, grad_bf16, stream);
+        if (e != hipSuccess) return e;
+        return launch_bwd_dk(q, k, v, lse, dout, delta, dk, B, Hq, Hkv, N, d, scale, causal, dropout, grad_bf16,
+                             stream);
+    }
+    return causal ? launch_dkdv_fused_t<128, true>(Q, K, V, lse, G, delta, dk, dv, B, Hq, Hkv, N, scale, dropout,
+                                                   grad_bf16, stream)
+                  : launch_dkdv_fused_t<128, false>(Q, K, V, lse, G, delta, dk, dv, B, Hq, Hkv, N, scale, dropout,
+                                                    grad_bf16, stream);
+}
+
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                          const float* delta, void* dq, int B, int Hq, int Hkv, int N, int d, float scale, bool causal,
                          const DropoutParams* dropout, bool grad_bf16, hipStream_t stream) {
@@ -617,9 +937,8 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            hipStream_t stream) {
     hipError_t e = launch_bwd_preprocess(o, dout, delta, B * Hq, N, d, stream);
     if (e != hipSuccess) return e;
-    e = launch_bwd_dv(q, k, lse, dout, dv, B, Hq, Hkv, N, d, scale, causal, dropout, grad_bf16, stream);
-    if (e != hipSuccess) return e;
-    e = launch_bwd_dk(q, k, v, lse, dout, delta, dk, B, Hq, Hkv, N, d, scale, causal, dropout, grad_bf16, stream);
+    e = launch_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, B, Hq, Hkv, N, d, scale, causal, dropout, grad_bf16,
+                        stream);
     if (e != hipSuccess) return e;
     return launch_bwd_dq(q, k, v, lse, dout, delta, dq, B, Hq, Hkv, N, d, scale, causal, dropout, grad_bf16, stream);
 }

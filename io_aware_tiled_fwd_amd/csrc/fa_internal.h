@@ -17,7 +17,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 // Forward, fp32 in/out (one key/value head per query head).
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
                           int N, int d, float scale, bool causal, hipStream_t stream);
-// Backward: preprocess (delta), dV, dK and dQ kernels, in stream order.
+// Backward: preprocess (delta), dK/dV and dQ kernels, in stream order.
 // dropout: null for none, else the forward's mask is regenerated.
 // grad_bf16: dq, dk, dv are bf16 (no dropout then), else fp32.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -34,6 +34,10 @@ hipError_t launch_bwd_dv(const void* q, const void* k, const float* lse, const v
 hipError_t launch_bwd_dk(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                          const float* delta, void* dk, int B, int Hq, int Hkv, int N, int d, float scale,
                          bool causal, const DropoutParams* dropout, bool grad_bf16, hipStream_t stream);
+// dK and dV together (one kernel of paired wavefronts; bitwise equal to the two above).
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                           const float* delta, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, float scale,
+                           bool causal, const DropoutParams* dropout, bool grad_bf16, hipStream_t stream);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                          const float* delta, void* dq, int B, int Hq, int Hkv, int N, int d, float scale,
                          bool causal, const DropoutParams* dropout, bool grad_bf16, hipStream_t stream);

@@ -21,7 +21,9 @@ def test_flop_counts():
     assert b == 2.5 * f
     k = bench.kernel_flops(2, 32, 8192, 128, True)
     assert k["fwd"] == f
-    assert k["bwd_dv"] + k["bwd_dk"] + k["bwd_dq"] == 4 * f  # 8 products run vs 5 counted
+    assert k["bwd_dkdv"] + k["bwd_dq"] == 3.5 * f  # 7 products run vs 5 counted
+    k64 = bench.kernel_flops(2, 32, 8192, 64, True)
+    assert k64["bwd_dkdv"] + k64["bwd_dq"] == 4 * k64["fwd"]  # separate dV and dK kernels at d = 64
 
 
 def test_cpu_baseline_runs_on_a_small_head():

@@ -28,6 +28,8 @@ NO_SPILL = [
     "fwd_bf16_kernelILi128ELb1ELb0E", "fwd_bf16_kernelILi128ELb0ELb0E",
     "fwd_bf16_kernelILi64ELb1ELb0E", "fwd_bf16_kernelILi64ELb0ELb0E",
     "fwd_bf16_kernelILi128ELb1ELb1E",
+    "bwd_dkdv_fused_kernelILi128ELb1ELb0ELb0EfE", "bwd_dkdv_fused_kernelILi128ELb0ELb0ELb0EfE",
+    "bwd_dkdv_fused_kernelILi128ELb1ELb1ELb0EfE", "bwd_dkdv_fused_kernelILi128ELb1ELb0ELb1EfE",
     "bwd_dkdv_kernelILi128ELb1ELb1ELb0ELb0EfE", "bwd_dkdv_kernelILi128ELb1ELb0ELb0ELb0EfE",
     "bwd_dq_kernelILi128ELb1ELb0EfE", "bwd_preprocess_kernelILi128E",
     "fwd_fp8_kernelILi128ELb1E", "decode_split_kernelILi128ELb1E", "decode_merge_kernelILi128E",

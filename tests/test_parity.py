@@ -312,19 +312,25 @@ def test_abi_errors_leave_outputs_untouched():
                        q[:, :, :, :96].contiguous(), o[:, :, :, :96].contiguous(), lse)
 
 
-def test_backward_stages_equal_fa_bwd():
-    """fa_bwd_preprocess, fa_bwd_dv, fa_bwd_dk, fa_bwd_dq in stream order are fa_bwd."""
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_stages_equal_fa_bwd(d):
+    """fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq in stream order are fa_bwd; the
+    one-gradient kernels (fa_bwd_dv, fa_bwd_dk) give the same dV and dK bitwise.
+    At d = 128 fa_bwd_dkdv is the paired-wavefront kernel, so this also checks
+    that P handed from one wavefront to its partner arrives intact, over
+    several key blocks, causal diagonal blocks and a ragged tail."""
     for causal in (False, True):
-        ts = inputs.normal_qkv(1, 3, 777, 128, 71, with_dout=True)
+        ts = inputs.normal_qkv(1, 3, 777, d, 71, with_dout=True)
         dev = upload(ts)
         o, lse = _fwd(dev, causal, None)
         dq, dk, dv = binding.attention_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], causal=causal)
         delta = torch.empty_like(lse)
-        sq, sk, sv = (torch.full_like(dq, float("nan")) for _ in range(3))
+        sq, sk, sv, ok, ov = (torch.full_like(dq, float("nan")) for _ in range(5))
         binding.fa_bwd_preprocess(o, dev["do"], delta)
-        binding.fa_bwd_dv(dev["q"], dev["k"], lse, dev["do"], sv, causal)
-        binding.fa_bwd_dk(dev["q"], dev["k"], dev["v"], lse, dev["do"], delta, sk, causal)
+        binding.fa_bwd_dkdv(dev["q"], dev["k"], dev["v"], lse, dev["do"], delta, sk, sv, causal)
         binding.fa_bwd_dq(dev["q"], dev["k"], dev["v"], lse, dev["do"], delta, sq, causal)
+        binding.fa_bwd_dv(dev["q"], dev["k"], lse, dev["do"], ov, causal)
+        binding.fa_bwd_dk(dev["q"], dev["k"], dev["v"], lse, dev["do"], delta, ok, causal)
         torch.cuda.synchronize()
-        for a, b in ((sq, dq), (sk, dk), (sv, dv)):
+        for a, b in ((sq, dq), (sk, dk), (sv, dv), (ok, dk), (ov, dv)):
             assert torch.equal(a, b)
