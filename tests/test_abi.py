@@ -110,6 +110,29 @@ def test_bwd_rejects_bad_arguments(lib):
     assert call(ptrs) == 1
 
 
+def test_bwd_stages_reject_bad_arguments(lib):
+    """The backward stage entry points check pointers, shapes and alignment
+    before any launch (fa_bwd_dkdv: q, k, v, lse, dO, delta, dk, dv)."""
+    ok = [FAKE] * 8
+
+    def dkdv(ptrs, B=1, H=1, N=16, d=128, scale=0.1):
+        return lib.fa_bwd_dkdv(*ptrs, B, H, N, d, ctypes.c_float(scale), 1, NUL)
+
+    for i in range(8):
+        ptrs = list(ok)
+        ptrs[i] = NUL
+        assert dkdv(ptrs) == 1
+    assert dkdv(ok, N=0) == 1
+    assert dkdv(ok, scale=float("nan")) == 1
+    assert dkdv(ok, d=96) == 2
+    ptrs = list(ok)
+    ptrs[7] = ctypes.c_void_p(0x1004)
+    assert dkdv(ptrs) == 1
+    assert lib.fa_bwd_dv(*([FAKE] * 4 + [NUL]), 1, 1, 16, 128, ctypes.c_float(0.1), 1, NUL) == 1
+    assert lib.fa_bwd_dk(*([FAKE] * 7), 1, 1, 16, 80, ctypes.c_float(0.1), 1, NUL) == 2
+    assert lib.fa_bwd_dq(*([FAKE] * 6 + [NUL]), 1, 1, 16, 128, ctypes.c_float(0.1), 1, NUL) == 1
+
+
 def test_gqa_rejects_bad_arguments(lib):
     """Grouped heads: Hkv must be >= 1 and divide Hq; the shape checks of the
     per-head entry points apply to Hq."""
