@@ -100,6 +100,34 @@ def test_c4_ragged_sampled_rows():
                f"c4 heads {heads}, {rows_in_head.size} rows each")
 
 
+def test_c3_causal_bwd_bench_shape_sampled_heads():
+    """The benchmark's step at its full size (B2 H32 N8192 d128, causal, the same
+    seeded inputs): the backward through fa_bwd (preprocess, the paired dK/dV
+    kernel, dQ), every gradient of two sampled heads against the oracle, and the
+    column-sum invariants on every head."""
+    w = inputs.WORKLOADS["c3_bf16_causal_n8192_d128"]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    ts = inputs.normal_qkv(B, H, N, d, w["seed"], with_dout=True)
+    scale = inputs.default_scale(d)
+    _say("c3 bwd: bf16 causal B2 H32 N8192 d128")
+    dev = upload(ts)
+    o, lse = _fwd(dev, True, scale)
+    dq, dk, dv = binding.attention_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], causal=True,
+                                       scale=scale)
+    torch.cuda.synchronize()
+    heads = inputs.sample_heads(B * H, 2, w["seed"] + 2000)
+    arr = {n: ts.f64[n].reshape(B * H, N, d) for n in ("q", "k", "v", "do")}
+    rq, rk, rv, _ = oracle.attn_bwd(*(arr[n][heads] for n in ("q", "k", "v", "do")), scale, causal=True)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        e = maxabs(f64(got).reshape(B * H, N, d)[heads], ref)
+        _say(f"c3 bwd heads {heads}: max|d{name}|={e:.3e}")
+        assert e <= TOL_BF16_GRAD, f"{name} error {e}"
+    sdk = dk.double().sum(2).abs().max().item()
+    sdv = (dv.double().sum(2) - dev["do"].double().sum(2)).abs().max().item()
+    _say(f"c3 bwd invariants all heads: max|sum dK|={sdk:.3e} max|sum dV - sum dO|={sdv:.3e}")
+    assert sdk <= 0.5 and sdv <= 0.5
+
+
 def test_c5_causal_fwd_bwd_sampled_heads():
     w = inputs.WORKLOADS["c5_bf16_causal_fwdbwd_n4096_d128"]
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
