@@ -177,6 +177,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
             if constexpr (DK)
                 vf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(vrs, (lq * D + 16 * ks + 8 * h) * 2, kw0 * D * 2));
         }
+        wait_vmem_loads();
     }
     f32x16 acc[D / 32];
 #pragma unroll
@@ -423,6 +424,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks)
             kvf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rs, (lq * D + 16 * ks + 8 * h) * 2, kw0 * D * 2));
+        wait_vmem_loads();
     }
     f32x16 acc[D / 32];
 #pragma unroll

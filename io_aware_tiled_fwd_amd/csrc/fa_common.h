@@ -211,6 +211,14 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
 __device__ __forceinline__ int thread_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
 __device__ __forceinline__ int block_id() { return (int)__builtin_amdgcn_workgroup_id_x(); }
 
+// Waits until every global and buffer load this wavefront has issued has
+// returned (s_waitcnt vmcnt(0)).  Called once after the loads of the
+// register-resident operands, before the tile loop: without it the compiler's
+// wait insertion, which does not know that those loads completed long before,
+// guards their uses inside the loop with counts that include the loop's own
+// prefetch loads, so a wavefront could stall on a prefetch it does not need yet.
+__device__ __forceinline__ void wait_vmem_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Index of the calling wavefront in its workgroup, as a scalar (wave-uniform)
 // value so that branches on it are scalar branches.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(thread_id() >> 6); }

@@ -82,6 +82,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
         qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(qrs, (lq * D + 16 * ks + 8 * h) * 2, qw0 * D * 2));
+    wait_vmem_loads();
 
     f32x16 oacc[NDB];
 #pragma unroll

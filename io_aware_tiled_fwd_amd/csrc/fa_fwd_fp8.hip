@@ -111,6 +111,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void fwd_fp8_kernel(
         const int off = lq * D + 64 * ks + 32 * h;
         qf[ks] = join8(buffer_load16(qrs, off, qw0 * D), buffer_load16(qrs, off + 16, qw0 * D));
     }
+    wait_vmem_loads();
 
     f32x16 oacc[NDB];
 #pragma unroll

@@ -69,6 +69,36 @@ def test_no_function_calls(code_objects):
         assert calls == 0, f"{co.name}: {calls} function calls (s_swappc_b64) in the kernels"
 
 
+# Kernels whose MFMAs must not wait on outstanding global loads: their
+# register-resident operands are waited for once before the tile loop, so a
+# vmcnt wait in front of an MFMA would mean a stall on a prefetch.
+NO_LOAD_WAIT = [
+    "fwd_bf16_kernelILi128ELb1ELb0E", "fwd_bf16_kernelILi128ELb0ELb0E",
+    "bwd_dkdv_fused_kernelILi128ELb1ELb0ELb0EfE", "bwd_dkdv_fused_kernelILi128ELb0ELb0ELb0EfE",
+]
+
+
+def test_mfmas_do_not_wait_on_loads(code_objects):
+    seen = set()
+    for co in code_objects:
+        dis = subprocess.run([TOOLS["llvm-objdump"], "-d", str(co)], capture_output=True, text=True, check=True).stdout
+        cur, prev = None, ""
+        for line in dis.splitlines():
+            m = re.match(r"^[0-9a-f]+ <(\S+)>:", line)
+            if m:
+                cur, prev = m.group(1), ""
+                continue
+            if cur is None or not any(f in cur for f in NO_LOAD_WAIT):
+                continue
+            seen.update(f for f in NO_LOAD_WAIT if f in cur)
+            ins = line.strip()
+            if ins.startswith("v_mfma"):
+                assert not (prev.startswith("s_waitcnt") and "vmcnt" in prev), f"{cur}: {prev} before {ins[:40]}"
+            if ins:
+                prev = ins
+    assert seen == set(NO_LOAD_WAIT), f"kernels not found: {set(NO_LOAD_WAIT) - seen}"
+
+
 def test_hot_kernels_do_not_spill(code_objects):
     spills = {}
     for co in code_objects:
