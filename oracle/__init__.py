@@ -23,14 +23,15 @@ Functions take and return numpy float64 arrays laid out ``[BH, N, d]``
   :func:`attn_fwd_rows_dropout` -- the same with dropout of the attention
   probabilities, the mask drawn from Philox4x32-10 by seed and offset (same
   page, "Implementation notes"); :func:`dropout_mask` and
-  :func:`dropout_bytes` expose the mask and the generator's bytes.  The
-  generator's exact output bits are parity unpinned (no published vector in
-  the pages; its statistics and the dropout arithmetic given the mask are
-  pinned).
-* :func:`attn_fwd_tiled` -- the per-query-block online-softmax loop of that
-  page with deferred normalisation, used only to show tiled == untiled; it can
-  trace the running (m, l, acc) of one row, which the worked example on the
-  "Flash Attention and Memory-Efficient Attention Variants" page prints.
+  :func:`dropout_bytes` expose the mask and the generator's bytes, and
+  :func:`philox4x32_10` the generator itself (pinned to the known-answer
+  vectors published with the generator's reference implementation).
+* :func:`attn_fwd_rows` -- the plain forward for listed query rows only.
+* :func:`attn_fwd_tiled` -- a tiled forward: each key block reduced to a
+  per-row summary, summaries folded with the online-softmax rescaling rule of
+  that page, one division at the end; used only to show tiled == untiled.  It
+  can trace the running (m, l, acc) of one row, which the worked example on
+  the "Flash Attention and Memory-Efficient Attention Variants" page prints.
 """
 from __future__ import annotations
 
@@ -95,6 +96,9 @@ def _load():
                                                                    ctypes.c_double, u64, u64, ctypes.c_int]
         lib.oracle_dropout_mask.argtypes = [u8p, _i64, _i64, ctypes.c_double, u64, u64]
         lib.oracle_dropout_bytes.argtypes = [u8p, _i64, _i64, u64, u64]
+        u32p = ctypes.POINTER(ctypes.c_uint32)
+        lib.oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
+        lib.oracle_philox4x32_10.restype = ctypes.c_int
         for fn in (lib.oracle_attn_fwd_dropout, lib.oracle_attn_bwd_dropout, lib.oracle_attn_fwd_rows_dropout,
                    lib.oracle_dropout_mask, lib.oracle_dropout_bytes):
             fn.restype = ctypes.c_int
@@ -349,3 +353,14 @@ def attn_fwd_rows(q, k, v, rows, scale, causal=False, threads=0):
                                         int(bool(causal)), _threads(threads)),
            "oracle_attn_fwd_rows")
     return o, lse
+
+
+def philox4x32_10(counter, key):
+    """Philox4x32-10 of four 32-bit counter words and two key words (Salmon,
+    Moraes, Dror and Shaw, SC 2011), the generator of the dropout mask.
+    Returns the four output words as Python ints."""
+    c = (ctypes.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in counter])
+    k = (ctypes.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    out = (ctypes.c_uint32 * 4)()
+    _check(_load().oracle_philox4x32_10(c, k, out), "oracle_philox4x32_10")
+    return [int(x) for x in out]

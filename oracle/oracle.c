@@ -5,11 +5,11 @@
  * benchmark's CPU-baseline leg load this library.  The GPU path never calls it
  * and shares no code with it.
  *
- * What it computes is the plain definition that FlashAttention reproduces
- * exactly (the pages state the tiled kernel returns "exactly the same result"
- * as standard attention; "FlashAttention Explained", section "Online
- * softmax"; "Flash Attention and Memory-Efficient Attention Variants",
- * worked example).  Per head, with S = scale * Q K^T:
+ * What it computes is the plain definition, which FlashAttention reaches
+ * without approximation: the tiled kernel and standard attention agree up to
+ * rounding ("FlashAttention Explained", section "Online softmax"; "Flash
+ * Attention and Memory-Efficient Attention Variants", worked example).  Per
+ * head, with S = scale * Q K^T:
  *
  *   P   = softmax(S) row-wise, over visible keys only
  *   O   = P V
@@ -22,12 +22,14 @@
  *   dV = P^T dO,   dP = dO V^T,   D_i = sum_t dO_it O_it,
  *   dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
  *
- * A second forward, oracle_attn_fwd_tiled, follows the per-query-block loop of
- * the same deep-dive page ("How it works": running row max m, running sum l,
- * rescale alpha = exp(m - m_new), deferred division by l) in fp64, so that
- * "tiled equals untiled" can be checked.  It also records the running state
- * of one chosen row after every key block, which the worked example on the
- * "Flash Attention and Memory-Efficient Attention Variants" page prints.
+ * A second forward, oracle_attn_fwd_tiled, reduces each block of keys to a
+ * per-row summary (block maximum, sum of exponentials, weighted sum of V) and
+ * folds the summaries together with the rescaling rule of the same deep-dive
+ * page ("How it works": running maximum and sum, rescale by exp(m_old - m_new),
+ * one division at the end), in fp64, so that tiled and untiled results can be
+ * compared.  It also records the running state of one chosen row after every
+ * key block, which the worked example on the "Flash Attention and
+ * Memory-Efficient Attention Variants" page prints.
  *
  * Layout: every tensor is row-major contiguous [BH, N, d] (lse/delta [BH, N]),
  * fp64.  Causal means key j is visible to query i iff j <= i (square,
@@ -134,8 +136,9 @@ static int visible(int causal, int64_t i, int64_t j) { return !causal || j <= i;
 /* and is kept when that byte is >= thr = floor(256 p + 1/2); kept           */
 /* probabilities are scaled by 256 / (256 - thr), so the drop probability is */
 /* thr / 256.  L and the softmax denominator are those of the undropped P.    */
-/* The generator's exact output bits are parity unpinned: the pages print no */
-/* Philox vector (its statistics and the dropout arithmetic are pinned).     */
+/* The pages print no Philox output; the generator is pinned to the known-   */
+/* answer vectors published with the Random123 reference implementation of  */
+/* the same paper (oracle_philox4x32_10 exports it for that check).          */
 
 typedef struct {
     int thr;           /* bytes below thr are dropped */
@@ -164,6 +167,13 @@ static void philox4x32_10(const uint32_t ctr[4], uint32_t k0, uint32_t k1, uint3
     out[1] = c1;
     out[2] = c2;
     out[3] = c3;
+}
+
+/* The generator itself, for its known-answer check: out = Philox4x32-10(ctr, key). */
+int oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    if (!ctr || !key || !out) return ORACLE_ERR_ARG;
+    philox4x32_10(ctr, key[0], key[1], out);
+    return ORACLE_OK;
 }
 
 static unsigned dropout_byte(const dropout_cfg* dc, int64_t bh, int64_t i, int64_t j) {
@@ -574,99 +584,124 @@ static int bwd_grouped(const double* q, const double* k, const double* v, const 
 }
 
 /* ------------------------------------------------------------------------ */
-/* Tiled forward with online softmax (deferred normalisation), in fp64.      */
+/* Tiled forward, in fp64: the keys are cut into blocks of bc, every block   */
+/* is reduced on its own to a summary of each query row, and the summaries   */
+/* are folded together with the online-softmax rescaling rule ("FlashAttention"
+ * deep-dive page, "How it works": running maximum, running sum, rescale by   */
+/* exp(m_old - m_new), one division at the end; the split-KV merge of its     */
+/* "Implementation notes" is the same rule).                                  */
 /*                                                                           */
-/* For each block of br query rows: m = -inf, l = 0, acc = 0; for each block */
-/* of bc keys: S = scale Q_i K_j^T (masked keys -> -inf), m_new = max(m,     */
-/* rowmax S), P = exp(S - m_new), alpha = exp(m - m_new) (0 while m = -inf),  */
-/* l = alpha l + rowsum P, acc = alpha acc + P V_j, m = m_new.  Finally       */
-/* O = acc / l and L = m + ln l.                                              */
+/* Summary of key block b for query row i (visible keys only):               */
+/*   mb = max_j s_ij,  lb = sum_j exp(s_ij - mb),  ab = sum_j exp(s_ij - mb) v_j */
+/* Folding (mb, lb, ab) into the row's running (M, Lam, A):                   */
+/*   M' = max(M, mb),  Lam' = exp(M - M') Lam + exp(mb - M') lb,              */
+/*   A' = exp(M - M') A + exp(mb - M') ab                                     */
+/* (a block with no visible key leaves the state as it is; the first block    */
+/* that has one sets it).  At the end O_i = A / Lam and L_i = M + ln Lam.     */
+/* Query rows are handled in groups of br; with exact arithmetic neither br   */
+/* nor bc changes the result.                                                 */
 /*                                                                           */
-/* trace (may be NULL) receives, for the query row trace_row of head 0, one  */
-/* record of 2 + d doubles per key block: m, l, acc[0..d-1].  It must hold   */
-/* ceil(N / bc) records.                                                      */
+/* trace (may be NULL) receives, for query row trace_row of head 0, the      */
+/* running state after each key block as 2 + d doubles: M, Lam, A[0..d-1].   */
+/* It must hold ceil(N / bc) records.                                        */
+
+typedef struct {
+    double mx, sum; /* block maximum (-inf: nothing visible) and sum of exp(s - mx) */
+    double* wv;     /* d values: sum of exp(s - mx) v_j */
+} block_summary;
+
+/* Summary of keys [j0, j1) of one head for query row i (q_row = Q_i). */
+static void summarise_block(const double* q_row, const double* kh, const double* vh, int64_t d, double scale,
+                            int causal, int64_t i, int64_t j0, int64_t j1, double* s_buf, block_summary* out) {
+    out->mx = -INFINITY;
+    for (int64_t j = j0; j < j1; ++j) {
+        s_buf[j - j0] = -INFINITY;
+        if (!visible(causal, i, j)) continue;
+        double dot = 0.0;
+        for (int64_t t = 0; t < d; ++t) dot += q_row[t] * kh[j * d + t];
+        s_buf[j - j0] = scale * dot;
+        if (s_buf[j - j0] > out->mx) out->mx = s_buf[j - j0];
+    }
+    out->sum = 0.0;
+    for (int64_t t = 0; t < d; ++t) out->wv[t] = 0.0;
+    if (out->mx == -INFINITY) return;
+    for (int64_t j = j0; j < j1; ++j) {
+        const double w = exp(s_buf[j - j0] - out->mx); /* exp(-inf) = 0 for masked keys */
+        out->sum += w;
+        for (int64_t t = 0; t < d; ++t) out->wv[t] += w * vh[j * d + t];
+    }
+}
+
+/* Fold a block summary into a running state (M, Lam, A). */
+static void fold_block(double* M, double* Lam, double* A, const block_summary* b, int64_t d) {
+    if (b->mx == -INFINITY) return;
+    if (*M == -INFINITY) {
+        *M = b->mx;
+        *Lam = b->sum;
+        for (int64_t t = 0; t < d; ++t) A[t] = b->wv[t];
+        return;
+    }
+    const double top = *M > b->mx ? *M : b->mx;
+    const double w_run = exp(*M - top), w_blk = exp(b->mx - top);
+    *Lam = w_run * *Lam + w_blk * b->sum;
+    for (int64_t t = 0; t < d; ++t) A[t] = w_run * A[t] + w_blk * b->wv[t];
+    *M = top;
+}
 
 int oracle_attn_fwd_tiled(const double* q, const double* k, const double* v, double* o, double* lse,
                           int64_t BH, int64_t N, int64_t d, double scale, int causal,
                           int64_t br, int64_t bc, int64_t trace_row, double* trace) {
     if (!q || !k || !v || !o || !lse || BH <= 0 || N <= 0 || d <= 0 || br <= 0 || bc <= 0)
         return ORACLE_ERR_ARG;
-    double* S = (double*)malloc(sizeof(double) * (size_t)(br * bc));
-    double* m = (double*)malloc(sizeof(double) * (size_t)br);
-    double* l = (double*)malloc(sizeof(double) * (size_t)br);
-    double* acc = (double*)malloc(sizeof(double) * (size_t)(br * d));
-    if (!S || !m || !l || !acc) {
-        free(S);
-        free(m);
-        free(l);
-        free(acc);
-        return ORACLE_ERR_NOMEM;
-    }
-    for (int64_t bh = 0; bh < BH; ++bh) {
+    /* running state of br rows: M[br], Lam[br], A[br * d]; one block summary */
+    double* M = (double*)malloc(sizeof(double) * (size_t)br);
+    double* Lam = (double*)malloc(sizeof(double) * (size_t)br);
+    double* A = (double*)malloc(sizeof(double) * (size_t)(br * d));
+    double* s_buf = (double*)malloc(sizeof(double) * (size_t)bc);
+    double* wv = (double*)malloc(sizeof(double) * (size_t)d);
+    int rc = ORACLE_OK;
+    if (!M || !Lam || !A || !s_buf || !wv) rc = ORACLE_ERR_NOMEM;
+    block_summary blk = {0.0, 0.0, wv};
+    for (int64_t bh = 0; bh < BH && rc == ORACLE_OK; ++bh) {
         const double* qh = q + bh * N * d;
         const double* kh = k + bh * N * d;
         const double* vh = v + bh * N * d;
-        for (int64_t i0 = 0; i0 < N; i0 += br) {
-            const int64_t rows = (N - i0 < br) ? N - i0 : br;
-            for (int64_t r = 0; r < rows; ++r) {
-                m[r] = -INFINITY;
-                l[r] = 0.0;
-                for (int64_t t = 0; t < d; ++t) acc[r * d + t] = 0.0;
+        for (int64_t g0 = 0; g0 < N; g0 += br) {
+            const int64_t g1 = g0 + br < N ? g0 + br : N;
+            for (int64_t i = g0; i < g1; ++i) {
+                M[i - g0] = -INFINITY;
+                Lam[i - g0] = 0.0;
+                for (int64_t t = 0; t < d; ++t) A[(i - g0) * d + t] = 0.0;
             }
-            for (int64_t j0 = 0, blk = 0; j0 < N; j0 += bc, ++blk) {
-                const int64_t cols = (N - j0 < bc) ? N - j0 : bc;
-                for (int64_t r = 0; r < rows; ++r) {
-                    const int64_t i = i0 + r;
-                    double rowmax = -INFINITY;
-                    for (int64_t cc = 0; cc < cols; ++cc) {
-                        const int64_t j = j0 + cc;
-                        double sv = -INFINITY;
-                        if (visible(causal, i, j)) {
-                            double dot = 0.0;
-                            for (int64_t t = 0; t < d; ++t) dot += qh[i * d + t] * kh[j * d + t];
-                            sv = scale * dot;
-                        }
-                        S[r * bc + cc] = sv;
-                        if (sv > rowmax) rowmax = sv;
-                    }
-                    const double m_new = m[r] > rowmax ? m[r] : rowmax;
-                    if (m_new != -INFINITY) { /* else: nothing visible yet */
-                        const double alpha = (m[r] == -INFINITY) ? 0.0 : exp(m[r] - m_new);
-                        double rowsum = 0.0;
-                        for (int64_t t = 0; t < d; ++t) acc[r * d + t] *= alpha;
-                        for (int64_t cc = 0; cc < cols; ++cc) {
-                            const double pv = exp(S[r * bc + cc] - m_new); /* exp(-inf) = 0 */
-                            rowsum += pv;
-                            for (int64_t t = 0; t < d; ++t) acc[r * d + t] += pv * vh[(j0 + cc) * d + t];
-                        }
-                        l[r] = alpha * l[r] + rowsum;
-                        m[r] = m_new;
-                    }
+            for (int64_t b = 0; b * bc < N; ++b) {
+                const int64_t j0 = b * bc, j1 = j0 + bc < N ? j0 + bc : N;
+                for (int64_t i = g0; i < g1; ++i) {
+                    double* Ai = A + (i - g0) * d;
+                    summarise_block(qh + i * d, kh, vh, d, scale, causal, i, j0, j1, s_buf, &blk);
+                    fold_block(&M[i - g0], &Lam[i - g0], Ai, &blk, d);
                     if (trace && bh == 0 && i == trace_row) {
-                        double* rec = trace + blk * (2 + d);
-                        rec[0] = m[r];
-                        rec[1] = l[r];
-                        for (int64_t t = 0; t < d; ++t) rec[2 + t] = acc[r * d + t];
+                        double* rec = trace + b * (2 + d);
+                        rec[0] = M[i - g0];
+                        rec[1] = Lam[i - g0];
+                        for (int64_t t = 0; t < d; ++t) rec[2 + t] = Ai[t];
                     }
                 }
             }
-            for (int64_t r = 0; r < rows; ++r) {
-                double* oi = o + (bh * N + i0 + r) * d;
-                if (m[r] == -INFINITY) {
-                    for (int64_t t = 0; t < d; ++t) oi[t] = 0.0;
-                    lse[bh * N + i0 + r] = -INFINITY;
-                } else {
-                    for (int64_t t = 0; t < d; ++t) oi[t] = acc[r * d + t] / l[r];
-                    lse[bh * N + i0 + r] = m[r] + log(l[r]);
-                }
+            for (int64_t i = g0; i < g1; ++i) {
+                double* oi = o + (bh * N + i) * d;
+                const double* Ai = A + (i - g0) * d;
+                const int none = M[i - g0] == -INFINITY; /* no visible key: O = 0, L = -inf */
+                for (int64_t t = 0; t < d; ++t) oi[t] = none ? 0.0 : Ai[t] / Lam[i - g0];
+                lse[bh * N + i] = none ? -INFINITY : M[i - g0] + log(Lam[i - g0]);
             }
         }
     }
-    free(S);
-    free(m);
-    free(l);
-    free(acc);
-    return ORACLE_OK;
+    free(M);
+    free(Lam);
+    free(A);
+    free(s_buf);
+    free(wv);
+    return rc;
 }
 
 int oracle_default_threads(void) { return resolve_threads(0); }
