@@ -10,8 +10,9 @@
  * computed tile by tile with an online softmax so that S and P never reach
  * HBM; only O and the per-row logsumexp L are written.  The interface and
  * outputs follow the "FlashAttention" deep-dive page (tirogla.com), section
- * "How it works": in Q, K, V of shape N x d per head; out O and one
- * logsumexp per row; no state between calls.  The backward recomputes P from
+ * "How it works": per head the caller supplies N x d matrices Q, K, V and
+ * receives O plus one logsumexp value per query row; no state is kept
+ * between calls.  The backward recomputes P from
  * L and forms dQ, dK, dV from D = rowsum(dO * O) and dS = P * (dP - D) (same
  * section).
  *
@@ -27,7 +28,11 @@
  *    bf16 outputs are rounded to nearest, ties to even.
  *  - causal != 0 applies the square, top-left aligned mask: key j is visible to
  *    query i iff j <= i.  Tiles entirely above the diagonal are skipped.
- *  - scale is a finite float >= 0; callers usually pass 1/sqrt(d).
+ *  - scale is any finite float, positive, negative or zero, with
+ *    |scale| * log2(e) finite in fp32; callers usually pass 1/sqrt(d).  (The
+ *    kernels fold the sign, or a zero, into one operand of S exactly, so the
+ *    scores are bitwise scale times the fp32 sum of products.)  The scaled
+ *    scores themselves must stay inside the fp32 range.
  *  - lse is the natural-log logsumexp of the SCALED scores (the value that the
  *    deep-dive page's pseudocode stores as L = m + log l).
  *  - Calls are asynchronous on `stream` (0 = the null stream); outputs are
@@ -53,8 +58,8 @@ extern "C" {
 
 typedef enum {
     FA_OK = 0,
-    FA_ERR_INVALID_ARG = 1, /* null pointer, B/H/N < 1, Hkv not dividing Hq, negative or non-finite scale,
-                               size overflow, decode workspace too small */
+    FA_ERR_INVALID_ARG = 1, /* null pointer, B/H/N < 1, Hkv not dividing Hq, scale not finite (or
+                               |scale| log2(e) overflowing fp32), size overflow, decode workspace too small */
     FA_ERR_UNSUPPORTED = 2, /* head dimension d not in {64, 128} */
     FA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
 } fa_status;
@@ -80,8 +85,8 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 
 /*
  * Attention dropout ("FlashAttention" deep-dive page, "Implementation notes":
- * the backward regenerates the mask from a Philox seed and offset rather than
- * storing it).  As fa_fwd_gqa / fa_bwd_gqa, with each attention probability
+ * the mask is never written out; the backward draws it again from a Philox
+ * seed and offset).  As fa_fwd_gqa / fa_bwd_gqa, with each attention probability
  * P_ij of flat query head bh = b*Hq + h dropped with probability thr/256 and
  * kept ones scaled by 256/(256 - thr), thr = min(255, floor(256 dropout_p + 1/2)):
  *   O = (P * Z) V,  Z_ij = keep_ij * 256/(256 - thr);  lse is that of the

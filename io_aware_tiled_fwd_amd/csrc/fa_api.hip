@@ -13,10 +13,15 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Any finite scale, of either sign or zero ("FlashAttention" deep-dive page,
+// "How it works": S = Q K^T times the scale), as long as the kernels' exponent
+// factor |scale| log2(e) is a finite fp32 value.
+bool scale_ok(float scale) { return isfinite(scale) && isfinite(fabsf(scale) * 1.4426950408889634f); }
+
 // Shared shape checks.  Returns FA_OK or the status to report.
 int check_shape(int B, int H, int N, int d, float scale) {
     if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
-    if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+    if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
     const int64_t bh = (int64_t)B * H;
     if (bh > INT32_MAX) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -126,7 +131,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     const float ds[] = {q_descale, k_descale, v_descale};
     for (float x : ds)
         if (!isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID_ARG;
-    if (!isfinite(scale * q_descale * k_descale * 1.4426950408889634f)) return FA_ERR_INVALID_ARG;
+    if (!isfinite(fabsf(scale) * q_descale * k_descale * 1.4426950408889634f)) return FA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
         return FA_ERR_INVALID_ARG;
     return from_hip(fa::launch_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, q_descale, k_descale, v_descale,
@@ -248,7 +253,7 @@ int fa_decode(const void* q, const void* k, const void* v, const int* kv_len, vo
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
     const int st = check_decode(B, Hq, Hkv, Nk, d, num_splits);
     if (st != FA_OK) return st;
-    if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+    if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
     if (kv_len && (reinterpret_cast<uintptr_t>(kv_len) & 3u) != 0) return FA_ERR_INVALID_ARG;
     const fa::DecodePlan p = fa::decode_plan(B, Hq, Hkv, Nk, num_splits);
@@ -262,7 +267,8 @@ const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "FA_OK";
         case FA_ERR_INVALID_ARG:
-            return "FA_ERR_INVALID_ARG: null pointer, misaligned pointer, bad size or head count, or non-finite scale";
+            return "FA_ERR_INVALID_ARG: null pointer, misaligned pointer, bad size or head count, or a scale whose "
+                   "magnitude times log2(e) is not a finite float";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
         case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error at launch";
         default: return "unknown fa_status";

@@ -137,8 +137,9 @@ template <int D, bool CAUSAL, bool DK, bool GROUPED, bool DROPOUT, typename OutT
 __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    OutT* __restrict__ dOut, int N, int BKV, int nkb, float scale_log2, float out_scale, int Hq, int G_arg,
+    OutT* __restrict__ dOut, int N, int BKV, int nkb, ScoreScale ss, float out_scale, int Hq, int G_arg,
     DropoutParams drop) {
+    const float scale_log2 = ss.c;
     const int G = GROUPED ? G_arg : 1;
     constexpr int BQ = kDkvBq;
     constexpr int RS = both_ways_stride<D>();
@@ -178,6 +179,10 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
                 vf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(vrs, (lq * D + 16 * ks + 8 * h) * 2, kw0 * D * 2));
         }
         wait_vmem_loads();
+        // The sign of the scale rides on K in S = Q K^T (ScoreScale); dK's own
+        // factor, out_scale, is the signed scale.
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) kf[ks] = apply_sign(kf[ks], ss);
     }
     f32x16 acc[D / 32];
 #pragma unroll
@@ -384,8 +389,9 @@ template <int D, bool CAUSAL, bool GROUPED, bool DROPOUT, typename OutT>
 __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    OutT* __restrict__ dKout, OutT* __restrict__ dVout, int N, int BKV, int nkb, float scale_log2, float dk_scale,
+    OutT* __restrict__ dKout, OutT* __restrict__ dVout, int N, int BKV, int nkb, ScoreScale ss, float dk_scale,
     float dv_scale, int Hq, int G_arg, DropoutParams drop) {
+    const float scale_log2 = ss.c;
     static_assert(D == 128, "the paired kernel is built for d = 128");
     const int G = GROUPED ? G_arg : 1;
     constexpr int BQ = kDkvBq;
@@ -425,6 +431,12 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
         for (int ks = 0; ks < D / 16; ++ks)
             kvf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(rs, (lq * D + 16 * ks + 8 * h) * 2, kw0 * D * 2));
         wait_vmem_loads();
+        // The dV wavefront's K carries the sign of the scale in S = Q K^T
+        // (ScoreScale); dk_scale is the signed scale.
+        if (dvw) {
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) kvf[ks] = apply_sign(kvf[ks], ss);
+        }
     }
     f32x16 acc[D / 32];
 #pragma unroll
@@ -644,8 +656,9 @@ template <int D, bool CAUSAL, bool DROPOUT, typename OutT>
 __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    OutT* __restrict__ dQ, int N, int BH, int nqb, float scale_log2, float scale, int Hq, int G,
+    OutT* __restrict__ dQ, int N, int BH, int nqb, ScoreScale ss, float scale, int Hq, int G,
     DropoutParams drop) {
+    const float scale_log2 = ss.c;
     constexpr int BKV = kDqBkv;
     constexpr int KS = both_ways_stride<D>();
     constexpr int VS = D + 8;  // rows only
@@ -698,6 +711,11 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
     stk.store(sK[0], KS);
     stv.store(sV[0], VS);
     __syncthreads();
+    // Q carries the sign of the scale in S^T = K Q^T (ScoreScale); the Q loads
+    // were issued before the first tile's and have landed by now.  dQ's own
+    // factor, `scale`, is the signed scale.
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = apply_sign(qf[ks], ss);
     // One key tile.  MASK masks keys past N and (causal) keys after the query;
     // only the tiles at the diagonal and the ragged end need it, and they come
     // last, so the loop is split and the other tiles carry no mask code.
@@ -791,10 +809,10 @@ hipError_t launch_dkdv_d(const bf16* q, const bf16* k, const bf16* v, const floa
     const float out_scale = DK ? scale : (DROPOUT ? dp.keep_scale : 1.0f);
     if (Hq == Hkv)
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK, false, DROPOUT, OutT>), grid, dim3(kBwdThreads), 0, stream,
-                           q, k, v, dout, lse, delta, out, N, BKV, nkb, scale * kLog2e, out_scale, Hq, 1, dp);
+                           q, k, v, dout, lse, delta, out, N, BKV, nkb, make_score_scale(scale, 1.f, 0x80008000u), out_scale, Hq, 1, dp);
     else
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, DK, true, DROPOUT, OutT>), grid, dim3(kBwdThreads), 0, stream,
-                           q, k, v, dout, lse, delta, out, N, BKV, nkb, scale * kLog2e, out_scale, Hq, Hq / Hkv, dp);
+                           q, k, v, dout, lse, delta, out, N, BKV, nkb, make_score_scale(scale, 1.f, 0x80008000u), out_scale, Hq, Hq / Hkv, dp);
     return hipGetLastError();
 }
 template <int D, bool CAUSAL, bool DROPOUT, typename OutT>
@@ -806,11 +824,11 @@ hipError_t launch_dkdv_fused_d(const bf16* q, const bf16* k, const bf16* v, cons
     const float dv_scale = DROPOUT ? dp.keep_scale : 1.0f;
     if (Hq == Hkv)
         hipLaunchKernelGGL((bwd_dkdv_fused_kernel<D, CAUSAL, false, DROPOUT, OutT>), grid, dim3(kBwdThreads), 0,
-                           stream, q, k, v, dout, lse, delta, dk, dv, N, BKV, nkb, scale * kLog2e, scale, dv_scale,
+                           stream, q, k, v, dout, lse, delta, dk, dv, N, BKV, nkb, make_score_scale(scale, 1.f, 0x80008000u), scale, dv_scale,
                            Hq, 1, dp);
     else
         hipLaunchKernelGGL((bwd_dkdv_fused_kernel<D, CAUSAL, true, DROPOUT, OutT>), grid, dim3(kBwdThreads), 0,
-                           stream, q, k, v, dout, lse, delta, dk, dv, N, BKV, nkb, scale * kLog2e, scale, dv_scale,
+                           stream, q, k, v, dout, lse, delta, dk, dv, N, BKV, nkb, make_score_scale(scale, 1.f, 0x80008000u), scale, dv_scale,
                            Hq, Hq / Hkv, dp);
     return hipGetLastError();
 }
@@ -850,15 +868,15 @@ hipError_t launch_dq_t(const bf16* q, const bf16* k, const bf16* v, const float*
     const dim3 grid(grid_for_tasks(nqb * BH));
     if (grad_bf16)
         hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, bf16>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                           lse, delta, static_cast<bf16*>(dq), N, BH, nqb, scale * kLog2e, scale, Hq, Hq / Hkv,
+                           lse, delta, static_cast<bf16*>(dq), N, BH, nqb, make_score_scale(scale, 1.f, 0x80008000u), scale, Hq, Hq / Hkv,
                            kNoDropout);
     else if (dropout)
         hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true, float>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                           lse, delta, static_cast<float*>(dq), N, BH, nqb, scale * kLog2e, scale, Hq, Hq / Hkv,
+                           lse, delta, static_cast<float*>(dq), N, BH, nqb, make_score_scale(scale, 1.f, 0x80008000u), scale, Hq, Hq / Hkv,
                            *dropout);
     else
         hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, float>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                           lse, delta, static_cast<float*>(dq), N, BH, nqb, scale * kLog2e, scale, Hq, Hq / Hkv,
+                           lse, delta, static_cast<float*>(dq), N, BH, nqb, make_score_scale(scale, 1.f, 0x80008000u), scale, Hq, Hq / Hkv,
                            kNoDropout);
     return hipGetLastError();
 }

@@ -109,6 +109,41 @@ __device__ __forceinline__ bool wg_coords(int id, int BH, int nqb, bool causal, 
     return true;
 }
 
+// Score scaling.  The method's scores are S = scale Q K^T for any finite
+// scale ("FlashAttention" deep-dive page, "How it works").  The kernels need
+// a positive factor c in P = 2^(s c - m): their row maxima are taken over the
+// unscaled products s, masked scores are -inf before the factor is applied,
+// and c = 0 would turn those into NaN.  The sign of the scale is therefore
+// moved into the operand that each kernel keeps in registers (Q, or K in the
+// dK/dV kernels): negating every element of one operand negates every product
+// exactly, so |scale| (-s) is bitwise scale * s.  A zero scale zeroes that
+// operand instead: every score is then exactly 0 = 0 * s, and c may be any
+// positive number.  The gradients' own factor (dQ = scale dS K, dK = scale
+// dS^T Q) keeps the signed scale.
+struct ScoreScale {
+    float c;        // positive factor of the log2-domain exponent: |scale| log2(e) (or log2(e) for scale 0)
+    uint32_t keep;  // AND mask applied to the register-resident operand's words (0: zero it)
+    uint32_t flip;  // then XOR mask: the sign bits of its elements when scale < 0, else 0
+};
+// sign_bits: the sign bits of one 32-bit word of the operand's element type
+// (0x80008000 for bf16 pairs, 0x80000000 for fp32, 0x80808080 for fp8 bytes);
+// extra: further positive factors of the exponent (fp8 dequantisation).
+inline ScoreScale make_score_scale(float scale, float extra, uint32_t sign_bits) {
+    const float c = __builtin_fabsf(scale) * extra * kLog2e;
+    if (scale == 0.f || c == 0.f) return ScoreScale{kLog2e, 0u, 0u};  // all scores exactly 0
+    return ScoreScale{c, 0xFFFFFFFFu, scale < 0.f ? sign_bits : 0u};
+}
+__device__ __forceinline__ uint32_t apply_sign(uint32_t w, const ScoreScale& ss) { return (w & ss.keep) ^ ss.flip; }
+__device__ __forceinline__ bf16x8 apply_sign(bf16x8 x, const ScoreScale& ss) {
+    u32x4 u = __builtin_bit_cast(u32x4, x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = apply_sign(u[e], ss);
+    return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ float apply_sign(float x, const ScoreScale& ss) {
+    return __uint_as_float(apply_sign(__float_as_uint(x), ss));
+}
+
 // Threshold (log2 units) by which a row's maximum must grow before the
 // accumulator is rescaled.  Any reference value m gives the same exact result
 // (O = acc / l and L = m + log2 l both carry it), so m may lag the true maximum:

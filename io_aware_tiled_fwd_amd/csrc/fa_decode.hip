@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const int* __restrict__ kv_len, float* __restrict__ part_acc, float* __restrict__ part_ml,
     bf16* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int Nk, int nqg, int splits, int chunk,
-    int tasks, int BHq, float scale_log2) {
+    int tasks, int BHq, ScoreScale ss) {
+    const float scale_log2 = ss.c;
     using L = DecLayout<D>;
     constexpr int NKS = D / 16;  // k-steps of S
     constexpr int NDB = D / 32;  // 32-dimension blocks of O
@@ -141,6 +142,10 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_split_kernel(
         load_tile(0);
         store_tile();
     }
+    // The sign of the scale rides on Q (ScoreScale); the Q loads were issued
+    // before the first tile's and have landed by now.
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = apply_sign(qf[ks], ss);
     for (int t = 0; t < my_tiles; ++t) {
         // The region is this wavefront's own: LDS operations of one wavefront
         // execute in order, so a fence at wavefront scope (no instruction)
@@ -341,18 +346,18 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const int*
     auto Kp = static_cast<const bf16*>(k);
     auto Vp = static_cast<const bf16*>(v);
     auto Op = static_cast<bf16*>(o);
-    const float sl2 = scale * kLog2e;
+    const ScoreScale ss = make_score_scale(scale, 1.f, 0x80008000u);
     const dim3 grid(grid_for_tasks(tasks)), mgrid((BHq + 3) / 4);
 #define FA_DEC_LAUNCH(DD)                                                                                       \
     do {                                                                                                        \
         if (plan.nqg == 1)                                                                                      \
             hipLaunchKernelGGL((decode_split_kernel<DD, true>), grid, dim3(kDecThreads), 0, stream, Qp, Kp, Vp,  \
                                kv_len, pacc, pml, Op, lse, Hq, Hkv, Nk, plan.nqg, plan.splits, plan.chunk, tasks, \
-                               BHq, sl2);                                                                       \
+                               BHq, ss);                                                                        \
         else                                                                                                    \
             hipLaunchKernelGGL((decode_split_kernel<DD, false>), grid, dim3(kDecThreads), 0, stream, Qp, Kp, Vp, \
                                kv_len, pacc, pml, Op, lse, Hq, Hkv, Nk, plan.nqg, plan.splits, plan.chunk, tasks, \
-                               BHq, sl2);                                                                       \
+                               BHq, ss);                                                                        \
         hipError_t e = hipGetLastError();                                                                       \
         if (e != hipSuccess || plan.splits == 1) return e;                                                      \
         hipLaunchKernelGGL((decode_merge_kernel<DD>), mgrid, dim3(256), 0, stream, pacc, pml, Op, lse, BHq,     \

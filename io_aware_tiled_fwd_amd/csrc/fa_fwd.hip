@@ -6,9 +6,10 @@
 // by alpha = exp(m - m_new), accumulate P V, and finally store O = acc / l and
 // L = m + log l.  Exponentials are taken in base 2 with log2(e) folded into the
 // scale, S, l and acc are fp32 and P is rounded to bf16 only for the P V product
-// (same page, "Implementation notes").  Causal masks skip key tiles entirely
-// above the diagonal and mask only the tiles that cross it, which come last in
-// the key loop (same page, "Implementation notes").  Keys past N are masked to
+// (same page, "Implementation notes").  Under a causal mask a key tile that
+// lies wholly past a wavefront's last query is never computed, and the masking
+// code runs only on the tiles the diagonal passes through, which the key loop
+// reaches last (same page, "Implementation notes").  Keys past N are masked to
 // -inf and query rows past N are computed on zeros and never stored (same
 // page, the Triton kernel under "Code").
 //
@@ -46,8 +47,9 @@ constexpr int kFwdBc = 64;              // keys per tile
 template <int D, bool CAUSAL, bool DROPOUT>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, float scale_log2, int Hq, int G,
+    bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, ScoreScale ss, int Hq, int G,
     DropoutParams dp) {
+    const float scale_log2 = ss.c;
     constexpr int BC = kFwdBc;
     constexpr int KS = D + 8;   // K row stride: 16 consecutive rows hit distinct banks (b128 reads)
     constexpr int VS = D + 32;   // V rows, read transposed: 4 rows x 64 B of a half wave on disjoint banks
@@ -77,12 +79,15 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_base, head_bytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_base, head_bytes);
 
-    // Q^T operand: k-step ks holds Q[qrow][16 ks + 8 h .. +7].
+    // Q^T operand: k-step ks holds Q[qrow][16 ks + 8 h .. +7], carrying the
+    // sign of the scale (ScoreScale).
     bf16x8 qf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
         qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(qrs, (lq * D + 16 * ks + 8 * h) * 2, qw0 * D * 2));
     wait_vmem_loads();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = apply_sign(qf[ks], ss);
 
     f32x16 oacc[NDB];
 #pragma unroll
@@ -247,7 +252,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, float scale_log2) {
+    float* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, ScoreScale ss) {
+    const float scale_log2 = ss.c;
     constexpr int BC = kFwdBc;
     constexpr int KS = D + 2;  // odd-pair stride: 32 rows x 2 columns hit distinct banks
     constexpr int VS = D + 8;  // rows 4 apart land 32 banks apart
@@ -269,7 +275,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_f32_kernel(
 
     float qf[D / 2];  // Q[qrow][2 ks + h]
 #pragma unroll
-    for (int ks = 0; ks < D / 2; ++ks) qf[ks] = qrow < N ? Q[base + (int64_t)qrow * D + 2 * ks + h] : 0.f;
+    for (int ks = 0; ks < D / 2; ++ks)
+        qf[ks] = apply_sign(qrow < N ? Q[base + (int64_t)qrow * D + 2 * ks + h] : 0.f, ss);
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -374,7 +381,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     const int BH = B * Hq, G = Hq / Hkv;
     const int nqb = (N + kFwdBr - 1) / kFwdBr;
     const int grid = grid_for_tasks(nqb * BH);
-    const float sl2 = scale * kLog2e;
+    const ScoreScale ss = make_score_scale(scale, 1.f, 0x80008000u);
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
     auto V = static_cast<const bf16*>(v);
@@ -383,7 +390,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 #define FA_FWD_LAUNCH(DD, CC, DR)                                                                          \
     do {                                                                                                   \
         hipLaunchKernelGGL((fwd_bf16_kernel<DD, CC, DR>), dim3(grid), dim3(kFwdThreads), 0, stream, Q, K, V, \
-                           Op, lse, N, BH, nqb, sl2, Hq, G, dp);                                           \
+                           Op, lse, N, BH, nqb, ss, Hq, G, dp);                                           \
         return hipGetLastError();                                                                          \
     } while (0)
 #define FA_FWD_DROP(DD, CC)             \
@@ -405,11 +412,11 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           int N, int d, float scale, bool causal, hipStream_t stream) {
     const int nqb = (N + kFwdBr - 1) / kFwdBr;
     const int grid = grid_for_tasks(nqb * BH);
-    const float sl2 = scale * kLog2e;
+    const ScoreScale ss = make_score_scale(scale, 1.f, 0x80000000u);
 #define FA_FWD_LAUNCH(DD, CC)                                                                        \
     do {                                                                                             \
         hipLaunchKernelGGL((fwd_f32_kernel<DD, CC>), dim3(grid), dim3(kFwdThreads), 0, stream, q, k, v, \
-                           o, lse, N, BH, nqb, sl2);                                                 \
+                           o, lse, N, BH, nqb, ss);                                                 \
         return hipGetLastError();                                                                    \
     } while (0)
     if (d == 64) {

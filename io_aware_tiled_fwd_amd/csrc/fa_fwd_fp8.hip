@@ -73,8 +73,9 @@ __device__ __forceinline__ i32x8 lds_read32(const uint8_t* p) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kF8Threads, 1) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, float scale_log2, float v_descale, int Hq,
+    bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, ScoreScale ss, float v_descale, int Hq,
     int G) {
+    const float scale_log2 = ss.c;
     constexpr int BC = kF8Bc;
     constexpr int KS = D + 16;   // K row stride (bytes): 16 consecutive rows hit distinct banks
     constexpr int VTS = BC + 16;  // V^T row stride (bytes), same property
@@ -112,6 +113,11 @@ __global__ __launch_bounds__(kF8Threads, 1) void fwd_fp8_kernel(
         qf[ks] = join8(buffer_load16(qrs, off, qw0 * D), buffer_load16(qrs, off + 16, qw0 * D));
     }
     wait_vmem_loads();
+    // The sign of the scale rides on Q (ScoreScale).
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (int)apply_sign((uint32_t)qf[ks][e], ss);
 
     f32x16 oacc[NDB];
 #pragma unroll
@@ -255,7 +261,7 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, 
     const int BH = B * Hq, G = Hq / Hkv;
     const int nqb = (N + kF8Br - 1) / kF8Br;
     const int grid = grid_for_tasks(nqb * BH);
-    const float sl2 = scale * q_descale * k_descale * kLog2e;
+    const ScoreScale ss = make_score_scale(scale, q_descale * k_descale, 0x80808080u);
     auto Qp = static_cast<const uint8_t*>(q);
     auto Kp = static_cast<const uint8_t*>(k);
     auto Vp = static_cast<const uint8_t*>(v);
@@ -263,7 +269,7 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, 
 #define FA_F8_LAUNCH(DD, CC)                                                                                 \
     do {                                                                                                     \
         hipLaunchKernelGGL((fwd_fp8_kernel<DD, CC>), dim3(grid), dim3(kF8Threads), 0, stream, Qp, Kp, Vp, Op, \
-                           lse, N, BH, nqb, sl2, v_descale, Hq, G);                                          \
+                           lse, N, BH, nqb, ss, v_descale, Hq, G);                                           \
         return hipGetLastError();                                                                            \
     } while (0)
     if (d == 64) {

@@ -80,7 +80,9 @@ def test_fwd_rejects_bad_arguments(lib, f32):
     assert _fwd(lib, ok, N=0, f32=f32) == 1
     assert _fwd(lib, ok, scale=float("nan"), f32=f32) == 1
     assert _fwd(lib, ok, scale=float("inf"), f32=f32) == 1
-    assert _fwd(lib, ok, scale=-0.125, f32=f32) == 1  # negative scales are rejected
+    # any finite scale is accepted unless |scale| log2(e) overflows fp32
+    assert _fwd(lib, ok, scale=3.0e38, f32=f32) == 1
+    assert _fwd(lib, ok, scale=-3.0e38, f32=f32) == 1
     assert _fwd(lib, ok, d=96, f32=f32) == 2
     assert _fwd(lib, ok, d=256, f32=f32) == 2
     assert _fwd(lib, ok, d=0, f32=f32) == 2
@@ -172,12 +174,13 @@ def test_fp8_rejects_bad_arguments(lib):
         assert call(ptrs) == 1
     assert call(ok, Hkv=3) == 1
     assert call(ok, d=96) == 2
-    assert call(ok, scale=-1.0) == 1
+    assert call(ok, scale=float("nan")) == 1
     for bad in (0.0, -0.5, float("nan"), float("inf")):
         assert call(ok, qd=bad) == 1
         assert call(ok, kd=bad) == 1
         assert call(ok, vd=bad) == 1
     assert call(ok, scale=1e30, qd=1e30, kd=1e30) == 1  # folded exponent scale overflows
+    assert call(ok, scale=-1e30, qd=1e30, kd=1e30) == 1
     ptrs = list(ok)
     ptrs[1] = ctypes.c_void_p(0x1001)
     assert call(ptrs) == 1
@@ -203,7 +206,7 @@ def test_dropout_rejects_bad_arguments(lib):
         assert call(ok, offset=2 ** 32) == 1
         assert call(ok, Hkv=3) == 1
         assert call(ok, d=96) == 2
-        assert call(ok, scale=-1.0) == 1
+        assert call(ok, scale=float("nan")) == 1
 
 
 def test_decode_plan(lib):
@@ -244,7 +247,7 @@ def test_decode_rejects_bad_arguments(lib):
     assert call(ok, Nk=0) == 1
     assert call(ok, d=96) == 2
     assert call(ok, scale=float("nan")) == 1
-    assert call(ok, scale=-0.5) == 1
+    assert call(ok, scale=-3.0e38) == 1
     assert call(ok, splits=-1) == 1
     assert call(ok, ws=NUL) == 1                  # 4 splits need a workspace
     assert call(ok, ws_bytes=4 * 8 * 130 * 4 - 4) == 1  # one float short

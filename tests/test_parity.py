@@ -33,6 +33,18 @@ def _check_fwd(o, lse, ref_o, ref_l, tol_o, tol_l, what):
     assert el <= tol_l, f"{what}: L error {el}"
 
 
+def _check_invariants(dk, dv, dout, what):
+    """On every head: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i, exact for the
+    exact gradients.  The kernels round P and dS to bf16 (relative 2^-9) and
+    take D from the bf16 O; the resulting per-key errors, of RMS about 1e-3 at
+    these shapes, are independent across keys, so over N <= 8192 keys the sums
+    stay near sqrt(N) * 1e-3 <= 0.09.  The bar is 0.1."""
+    sdk = dk.double().sum(2).abs().max().item()
+    sdv = (dv.double().sum(2) - dout.double().sum(2)).abs().max().item()
+    _say(f"{what} invariants all heads: max|sum dK|={sdk:.3e} max|sum dV - sum dO|={sdv:.3e}")
+    assert sdk <= 0.1 and sdv <= 0.1
+
+
 # --- the five workloads ------------------------------------------------------
 
 def test_c1_fp32_single_head():
@@ -80,7 +92,9 @@ def test_c3_causal_sampled_heads():
     assert maxabs(lf[:, 0], l0) <= TOL_BF16_L
 
 
-def test_c4_ragged_sampled_rows():
+def test_c4_ragged_sampled_heads():
+    """Workload 4 (N = 18000, not a multiple of any tile): four sampled heads,
+    every row, against the oracle."""
     w = inputs.WORKLOADS["c4_bf16_n18000_d128"]
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     ts = inputs.normal_qkv(B, H, N, d, w["seed"])
@@ -89,22 +103,20 @@ def test_c4_ragged_sampled_rows():
     o, lse = _fwd(upload(ts), False, scale)
     torch.cuda.synchronize()
     heads = inputs.sample_heads(B * H, 4, w["seed"] + 1000)
-    rng = np.random.default_rng(w["seed"] + 2000)
-    rows_in_head = np.unique(np.concatenate([[0, 1, 127, 128], np.arange(N - 100, N),
-                                             rng.choice(N, 400, replace=False)]))
-    rows = np.concatenate([h * N + rows_in_head for h in heads])
     qkv = [ts.f64[n].reshape(B * H, N, d) for n in "qkv"]
-    ref_o, ref_l = oracle.attn_fwd_rows(*qkv, rows, scale)
-    of, lf = f64(o).reshape(-1, d), f64(lse).reshape(-1)
-    _check_fwd(of[rows], lf[rows], ref_o, ref_l, TOL_BF16_O, TOL_BF16_L,
-               f"c4 heads {heads}, {rows_in_head.size} rows each")
+    ref_o, ref_l = oracle.attn_fwd(*(x[heads] for x in qkv), scale)
+    _check_fwd(f64(o).reshape(B * H, N, d)[heads], f64(lse).reshape(B * H, N)[heads], ref_o, ref_l, TOL_BF16_O,
+               TOL_BF16_L, f"c4 heads {heads}, all {N} rows")
 
 
 def test_c3_causal_bwd_bench_shape_sampled_heads():
     """The benchmark's step at its full size (B2 H32 N8192 d128, causal, the same
     seeded inputs): the backward through fa_bwd (preprocess, the paired dK/dV
-    kernel, dQ), every gradient of two sampled heads against the oracle, and the
-    column-sum invariants on every head."""
+    kernel, dQ), every gradient of four sampled heads against the oracle; on
+    every head the paired kernel's dK and dV equal, bitwise, those of the two
+    one-gradient kernels (fa_bwd_dk, fa_bwd_dv), which compute P themselves, so
+    a P hand-over error on any head would show; and the column-sum
+    invariants."""
     w = inputs.WORKLOADS["c3_bf16_causal_n8192_d128"]
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     ts = inputs.normal_qkv(B, H, N, d, w["seed"], with_dout=True)
@@ -115,17 +127,22 @@ def test_c3_causal_bwd_bench_shape_sampled_heads():
     dq, dk, dv = binding.attention_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], causal=True,
                                        scale=scale)
     torch.cuda.synchronize()
-    heads = inputs.sample_heads(B * H, 2, w["seed"] + 2000)
+    delta = torch.empty_like(lse)
+    sk, sv = torch.full_like(dk, float("nan")), torch.full_like(dv, float("nan"))
+    binding.fa_bwd_preprocess(o, dev["do"], delta)
+    binding.fa_bwd_dk(dev["q"], dev["k"], dev["v"], lse, dev["do"], delta, sk, True, scale)
+    binding.fa_bwd_dv(dev["q"], dev["k"], lse, dev["do"], sv, True, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(sk, dk) and torch.equal(sv, dv), "paired dK/dV kernel differs from the one-gradient kernels"
+    del sk, sv
+    heads = inputs.sample_heads(B * H, 4, w["seed"] + 2000)
     arr = {n: ts.f64[n].reshape(B * H, N, d) for n in ("q", "k", "v", "do")}
     rq, rk, rv, _ = oracle.attn_bwd(*(arr[n][heads] for n in ("q", "k", "v", "do")), scale, causal=True)
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         e = maxabs(f64(got).reshape(B * H, N, d)[heads], ref)
         _say(f"c3 bwd heads {heads}: max|d{name}|={e:.3e}")
         assert e <= TOL_BF16_GRAD, f"{name} error {e}"
-    sdk = dk.double().sum(2).abs().max().item()
-    sdv = (dv.double().sum(2) - dev["do"].double().sum(2)).abs().max().item()
-    _say(f"c3 bwd invariants all heads: max|sum dK|={sdk:.3e} max|sum dV - sum dO|={sdv:.3e}")
-    assert sdk <= 0.5 and sdv <= 0.5
+    _check_invariants(dk, dv, dev["do"], "c3 bwd")
 
 
 def test_c5_causal_fwd_bwd_sampled_heads():
@@ -144,18 +161,12 @@ def test_c5_causal_fwd_bwd_sampled_heads():
     ref_o, ref_l = oracle.attn_fwd(*(arr[n][heads] for n in "qkv"), scale, causal=True)
     _check_fwd(f64(o).reshape(B * H, N, d)[heads], f64(lse).reshape(B * H, N)[heads], ref_o, ref_l,
                TOL_BF16_O, TOL_BF16_L, f"c5 fwd heads {heads}")
-    bheads = heads[:2]
-    rq, rk, rv, _ = oracle.attn_bwd(*(arr[n][bheads] for n in ("q", "k", "v", "do")), scale, causal=True)
+    rq, rk, rv, _ = oracle.attn_bwd(*(arr[n][heads] for n in ("q", "k", "v", "do")), scale, causal=True)
     for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-        e = maxabs(f64(got).reshape(B * H, N, d)[bheads], ref)
-        _say(f"c5 bwd heads {bheads}: max|d{name}|={e:.3e}")
+        e = maxabs(f64(got).reshape(B * H, N, d)[heads], ref)
+        _say(f"c5 bwd heads {heads}: max|d{name}|={e:.3e}")
         assert e <= TOL_BF16_GRAD, f"{name} error {e}"
-    # every head: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i (exact for the exact
-    # gradients; here up to the kernels' rounding)
-    sdk = dk.double().sum(2).abs().max().item()
-    sdv = (dv.double().sum(2) - dev["do"].double().sum(2)).abs().max().item()
-    _say(f"c5 invariants all heads: max|sum dK|={sdk:.3e} max|sum dV - sum dO|={sdv:.3e}")
-    assert sdk <= 0.5 and sdv <= 0.5
+    _check_invariants(dk, dv, dev["do"], "c5")
 
 
 # --- small and ragged shapes ----------------------------------------------------
@@ -307,14 +318,26 @@ def test_large_scores_stress():
 
 # --- determinism and the ABI on the device ----------------------------------------
 
-def test_bitwise_reproducible():
-    ts = inputs.normal_qkv(2, 4, 1000, 128, 61, with_dout=True)
-    dev = upload(ts)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bitwise_reproducible(d, causal):
+    """Two runs give bitwise equal outputs (no atomics, and no read of an LDS
+    buffer while it is being refilled): per-head and grouped (Hq 4 / Hkv 2)
+    forward and backward, and the fp8 forward."""
+    ts = inputs.normal_qkv(2, 4, 1000, d, 61, with_dout=True)
+    tg = inputs.normal_gqa(2, 4, 2, 1000, d, 62, with_dout=True)
+    t8 = inputs.fp8_qkv(2, 4, 2, 1000, d, 63)
+    dev, deg, de8 = upload(ts), upload(tg), upload(t8)
     runs = []
     for _ in range(2):
-        o, lse = _fwd(dev, True, None)
-        grads = binding.attention_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], causal=True)
-        runs.append([o, lse, *grads])
+        out = []
+        for x in (dev, deg):
+            o, lse = _fwd(x, causal, None)
+            grads = binding.attention_bwd(x["q"], x["k"], x["v"], o, lse, x["do"], causal=causal)
+            out += [o, lse, *grads]
+        out += list(binding.attention_fwd_fp8(de8["q"], de8["k"], de8["v"], t8.descale["q"], t8.descale["k"],
+                                              t8.descale["v"], causal=causal))
+        runs.append(out)
     torch.cuda.synchronize()
     for a, b in zip(*runs):
         assert torch.equal(a, b)
