@@ -61,7 +61,8 @@ typedef enum {
     FA_ERR_INVALID_ARG = 1, /* null pointer, B/H/N < 1, Hkv not dividing Hq, scale not finite (or
                                |scale| log2(e) overflowing fp32), size overflow, decode workspace too small */
     FA_ERR_UNSUPPORTED = 2, /* head dimension d not in {64, 128} */
-    FA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+    FA_ERR_HIP = 3,         /* the HIP runtime reported an error at launch */
+    FA_ERR_SCRATCH = 4      /* fa_bwd_noalloc: B*H*N exceeds FA_NOALLOC_MAX_ROWS */
 } fa_status;
 
 /*
@@ -239,6 +240,26 @@ int fa_bwd_dk(const void* q, const void* k, const void* v, const float* lse, con
 int fa_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dO,
               const float* delta, float* dq, int B, int H, int N, int d, float scale, int causal,
               hipStream_t stream);
+
+/*
+ * fa_bwd without the delta workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  The library keeps D = rowsum(dO * O)
+ * in a static device array of FA_NOALLOC_MAX_ROWS floats (16 MiB), one per
+ * GPU it runs on, held until the process ends; the call allocates nothing and
+ * calls no allocating routine.  Every other argument, and the results
+ * (bitwise those of fa_bwd), are as for fa_bwd.
+ *   Limit: B*H*N <= FA_NOALLOC_MAX_ROWS, else FA_ERR_SCRATCH before any launch.
+ *   The array of the CURRENT device (hipGetDevice) is used: `stream` must
+ *   belong to that device.  The first call on a device looks the array's
+ *   address up (hipGetSymbolAddress); a failure there returns FA_ERR_HIP.
+ *   Calls that overlap on one GPU (other streams, other host threads) share
+ *   the array and race: serialise them, e.g. on one stream.
+ */
+#define FA_NOALLOC_MAX_ROWS (1 << 22)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, float* dq, float* dk, float* dv,
+                   int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* fa_status_string(int status);

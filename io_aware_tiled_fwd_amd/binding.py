@@ -20,11 +20,12 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_SCRATCH = 0, 1, 2, 3, 4
+NOALLOC_MAX_ROWS = 1 << 22  # FA_NOALLOC_MAX_ROWS of include/fa.h
 SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_fwd_gqa", "fa_bwd_gqa", "fa_bwd_gqa_bf16grad",
            "fa_fwd_dropout",
            "fa_bwd_dropout", "fa_decode_plan", "fa_decode", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dv",
-           "fa_bwd_dk", "fa_bwd_dq", "fa_status_string", "fa_probe_mfma", "fa_probe_hbm_read")
+           "fa_bwd_dk", "fa_bwd_dq", "fa_status_string", "fa_probe_mfma", "fa_probe_hbm_read", "fa_bwd_noalloc")
 
 
 class FaError(RuntimeError):
@@ -50,6 +51,7 @@ def load_library():
     lib.fa_fwd.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_fwd_f32.argtypes = [vp] * 5 + [i, i, i, i, f, i, vp]
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
+    lib.fa_bwd_noalloc.argtypes = [vp] * 9 + [i, i, i, i, f, i, vp]
     lib.fa_fwd_gqa.argtypes = [vp] * 5 + [i, i, i, i, i, f, i, vp]
     lib.fa_bwd_gqa.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp]
     lib.fa_fwd_fp8.argtypes = [vp] * 5 + [i, i, i, i, i, f, f, f, f, i, vp]
@@ -69,7 +71,7 @@ def load_library():
     for fn in (lib.fa_fwd, lib.fa_fwd_f32, lib.fa_fwd_fp8, lib.fa_fwd_dropout, lib.fa_bwd_dropout,
                lib.fa_bwd_gqa_bf16grad, lib.fa_bwd, lib.fa_fwd_gqa, lib.fa_bwd_gqa, lib.fa_decode_plan,
                lib.fa_decode, lib.fa_bwd_preprocess, lib.fa_bwd_dkdv, lib.fa_bwd_dv, lib.fa_bwd_dk, lib.fa_bwd_dq,
-               lib.fa_probe_mfma, lib.fa_probe_hbm_read):
+               lib.fa_probe_mfma, lib.fa_probe_hbm_read, lib.fa_bwd_noalloc):
         fn.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -167,6 +169,29 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, causal=False, scale=None, s
                                ctypes.c_void_p(_stream_handle(stream)))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal=False, scale=None, stream=None) -> None:
+    """fa_bwd without the delta workspace: the library keeps D in its static
+    per-GPU array (B*H*N <= NOALLOC_MAX_ROWS) and allocates nothing."""
+    B, H, N, d = _shape(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check4(t, n, torch.bfloat16)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{n} must have shape {(B, H, N, d)}")
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check4(t, n, torch.float32)
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{n} must have shape {(B, H, N, d)}")
+    _check4(lse, "lse", torch.float32)
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError(f"lse must have shape {(B, H, N)}")
+    sc = _default_scale(d) if scale is None else float(scale)
+    st = load_library().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), B, H, N, d, sc, int(bool(causal)),
+                                       ctypes.c_void_p(_stream_handle(stream)))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_noalloc")
 
 
 def _gqa_shapes(q, k):

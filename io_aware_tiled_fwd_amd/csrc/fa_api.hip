@@ -6,8 +6,18 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_internal.h"
+
+// Static workspace of fa_bwd_noalloc: the backward's D = rowsum(dO * O) for up
+// to FA_NOALLOC_MAX_ROWS rows (16 MiB), in the library's own device memory so
+// that the entry point allocates nothing.  Each GPU the library runs on holds
+// its own copy until the process ends.  Host code must never use this name as
+// a device address (it is a host-side stand-in); it uses the address that
+// hipGetSymbolAddress reports for the current device (noalloc_scratch below).
+static __device__ __align__(256) float scratch[FA_NOALLOC_MAX_ROWS];
 
 namespace {
 
@@ -70,6 +80,25 @@ fa::DropoutParams dropout_params(float p, unsigned long long seed, unsigned long
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(float** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_HIP;
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return FA_OK;
+}
 
 }  // namespace
 
@@ -182,6 +211,25 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
     return fa_bwd_gqa(q, k, v, o, lse, dO, dq, dk, dv, delta, B, H, H, N, d, scale, causal, stream);
 }
 
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                   float* dq, float* dk, float* dv, int B, int H, int N, int d, float scale, int causal,
+                   hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+    const int st = check_shape(B, H, N, d, scale);
+    if (st != FA_OK) return st;
+    const void* ptrs[] = {q, k, v, o, lse, dO, dq, dk, dv};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+    if ((int64_t)B * H * N > (int64_t)FA_NOALLOC_MAX_ROWS) return FA_ERR_SCRATCH;
+    float* delta = nullptr;
+    const int sst = noalloc_scratch(&delta);
+    if (sst != FA_OK) return sst;
+    // Every element of delta that the kernels read is written by the
+    // preprocess kernel first, in stream order, so nothing needs clearing.
+    return from_hip(fa::launch_bwd_bf16(q, k, v, o, lse, dO, dq, dk, dv, delta, B, H, H, N, d, scale, causal != 0,
+                                        nullptr, false, stream));
+}
+
 int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H, int N, int d,
                       hipStream_t stream) {
     if (!o || !dO || !delta) return FA_ERR_INVALID_ARG;
@@ -271,6 +319,8 @@ const char* fa_status_string(int status) {
                    "magnitude times log2(e) is not a finite float";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dimension must be 64 or 128";
         case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error at launch";
+        case FA_ERR_SCRATCH:
+            return "FA_ERR_SCRATCH: B*H*N exceeds the static workspace of fa_bwd_noalloc (FA_NOALLOC_MAX_ROWS rows)";
         default: return "unknown fa_status";
     }
 }

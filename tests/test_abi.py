@@ -52,7 +52,7 @@ def test_binding_names_match_header():
 def test_status_strings(lib):
     from io_aware_tiled_fwd_amd import binding
     assert binding.fa_status_string(0) == "FA_OK"
-    for st in (1, 2, 3):
+    for st in (1, 2, 3, 4):
         assert binding.fa_status_string(st).startswith("FA_ERR_")
     assert "unknown" in binding.fa_status_string(99)
 
@@ -292,3 +292,26 @@ def test_probe_rejections(lib):
     assert lib.fa_probe_hbm_read(sink, 0, sink, None) == FA_ERR_INVALID_ARG
     assert lib.fa_probe_hbm_read(None, unit, sink, None) == FA_ERR_INVALID_ARG
     assert lib.fa_probe_hbm_read(ctypes.c_void_p(0x1008), unit, sink, None) == FA_ERR_INVALID_ARG
+
+
+def test_bwd_noalloc_rejects_bad_arguments(lib):
+    """fa_bwd_noalloc: the argument checks of fa_bwd, plus FA_ERR_SCRATCH when
+    B*H*N exceeds its static workspace -- all before any HIP call."""
+    from io_aware_tiled_fwd_amd import binding
+    ok = [FAKE] * 9
+
+    def call(ptrs, B=1, H=1, N=16, d=128, scale=0.1):
+        return lib.fa_bwd_noalloc(*ptrs, B, H, N, d, ctypes.c_float(scale), 1, NUL)
+
+    for i in range(9):
+        ptrs = list(ok)
+        ptrs[i] = NUL
+        assert call(ptrs) == 1
+    assert call(ok, N=0) == 1
+    assert call(ok, d=96) == 2
+    assert call(ok, scale=float("nan")) == 1
+    ptrs = list(ok)
+    ptrs[3] = ctypes.c_void_p(0x1004)
+    assert call(ptrs) == 1
+    assert call(ok, B=1, H=1, N=binding.NOALLOC_MAX_ROWS + 1, d=64) == 4
+    assert call(ok, B=4, H=32, N=binding.NOALLOC_MAX_ROWS // 64, d=128) == 4

@@ -62,11 +62,15 @@ def code_objects(tmp_path_factory):
 
 
 def test_no_function_calls(code_objects):
+    with_kernels = 0
     for co in code_objects:
         dis = subprocess.run([TOOLS["llvm-objdump"], "-d", str(co)], capture_output=True, text=True, check=True).stdout
-        assert "v_mfma" in dis or "s_endpgm" in dis, "disassembly looks empty"
+        if "s_endpgm" not in dis:
+            continue  # a code object with device data only (the static workspace of fa_api.hip)
+        with_kernels += 1
         calls = dis.count("s_swappc_b64")
         assert calls == 0, f"{co.name}: {calls} function calls (s_swappc_b64) in the kernels"
+    assert with_kernels >= 5, "fewer kernel code objects than sources with kernels"
 
 
 # Kernels whose MFMAs must not wait on outstanding global loads: their
