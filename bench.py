@@ -14,6 +14,7 @@ Counted FLOPs: forward 4 N^2 d B H, backward 10 N^2 d B H (2.5x forward), both
 halved under a causal mask.  Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--decode NAME|none] [--no-cpu-baseline]
+    python bench.py --configs   # one JSON line: every configuration's kernel times, plus the oracle's
 """
 from __future__ import annotations
 
@@ -30,6 +31,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (256 CUs x 2.4 GHz x 4096 FLOP/clk)
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
+PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector (the fp32 forward runs on fp32 MFMA, whose dense peak is the same)
 KERNEL_SOURCES = ("io_aware_tiled_fwd_amd/csrc/fa_fwd.hip", "io_aware_tiled_fwd_amd/csrc/fa_bwd.hip",
                   "io_aware_tiled_fwd_amd/csrc/fa_common.h")
 # Split-KV decode leg: one new token of a Llama-3-70B-like attention layer
@@ -283,6 +285,76 @@ def probe_leg(mfma_blocks=1024, mfma_iters=2000, read_mib=1024, reps=3):
                    f"{nbytes >> 20} MiB read once with 16-byte non-temporal loads (fa_probe.h)"}
 
 
+def config_table(iters=20, warmup=5, oracle=True):
+    """Every workload of the parity tests (inputs.WORKLOADS: the five configurations),
+    each on its own seeded inputs: GPU time of the forward (and of the backward
+    where the workload has one, plus the causal B2 H32 N8192 backward), the
+    counted TFLOP/s and fraction of the 2.5 PF bf16 peak; beside it the oracle's
+    time on a sample of the same inputs (all heads of the two small workloads,
+    the parity tests' four sampled heads otherwise), with the full-workload time
+    extrapolated by head count.  Returns {workload: {...}}."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from io_aware_tiled_fwd_amd import binding, inputs
+
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, w in inputs.WORKLOADS.items():
+        B, H, N, d, causal, dt = w["B"], w["H"], w["N"], w["d"], w["causal"], w["dtype"]
+        with_bwd = bool(w.get("backward")) or name.startswith("c3")
+        ts = inputs.normal_qkv(B, H, N, d, w["seed"], dtype=dt, with_dout=with_bwd and dt == "bf16")
+        if dt == "bf16":
+            t = {n: torch.from_numpy(ts.bits[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ts.names}
+        else:
+            t = {n: torch.from_numpy(ts.bits[n]).cuda() for n in ts.names}
+        scale = inputs.default_scale(d)
+        o = torch.empty_like(t["q"])
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        fwd = binding.fa_fwd_f32 if dt == "f32" else binding.fa_fwd
+        calls = [lambda: fwd(t["q"], t["k"], t["v"], o, lse, causal, scale, stream)]
+        if with_bwd:
+            g = [torch.empty((B, H, N, d), dtype=torch.float32, device="cuda") for _ in range(3)]
+            delta = torch.empty_like(lse)
+            calls.append(lambda: binding.fa_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], *g, delta, causal, scale,
+                                                stream))
+        for _ in range(warmup):
+            for c in calls:
+                c()
+        meds, _ = timed_rounds(calls, iters)
+        ff, fb = counted_flops(B, H, N, d, causal)
+        rec = {"B": B, "H": H, "N": N, "d": d, "causal": causal, "dtype": dt,
+               "fwd_ms": round(meds[0], 4), "fwd_tflops": round(ff / (meds[0] / 1e3) / 1e12, 2),
+               "fwd_frac_peak": None if dt == "f32" else round(ff / (meds[0] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        if dt == "f32":
+            rec["fwd_frac_peak_fp32"] = round(ff / (meds[0] / 1e3) / 1e12 / PEAK_F32_TFLOPS, 4)
+        if with_bwd:
+            rec.update({"bwd_ms": round(meds[1], 4), "bwd_tflops": round(fb / (meds[1] / 1e3) / 1e12, 2),
+                        "bwd_frac_peak": round(fb / (meds[1] / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+        del t, o, lse, calls
+        if with_bwd:
+            del g, delta
+        torch.cuda.empty_cache()
+        if oracle:
+            heads = list(range(B * H)) if B * H <= 64 and N <= 2048 else inputs.sample_heads(B * H, 4, w["seed"] + 1000)
+            arr = {n: ts.f64[n].reshape(B * H, N, d)[heads] for n in ts.names}
+            t0 = time.perf_counter()
+            oracle.attn_fwd(arr["q"], arr["k"], arr["v"], scale, causal)
+            t1 = time.perf_counter()
+            rec["oracle_fwd_s"] = round(t1 - t0, 3)
+            if with_bwd:
+                oracle.attn_bwd(arr["q"], arr["k"], arr["v"], arr["do"], scale, causal)
+                rec["oracle_bwd_s"] = round(time.perf_counter() - t1, 3)
+            rec["oracle_heads"] = len(heads)
+            rec["oracle_full_s"] = round((time.perf_counter() - t0) * (B * H) / len(heads), 1)
+            rec["oracle_threads"] = oracle.default_threads()
+        del ts
+        out[name] = rec
+        print(json.dumps({name: rec}), file=sys.stderr, flush=True)
+    return out
+
+
 def cpu_baseline(heads, causal):
     """The fp64 oracle, as it stands, on host cores: forward + backward of the
     first few heads of the benchmark's own inputs (batch 0), each over all N
@@ -321,6 +393,9 @@ def main(argv=None):
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 forward leg")
     ap.add_argument("--no-dropout", action="store_true", help="skip the dropout fwd+bwd leg")
     ap.add_argument("--no-probe", action="store_true", help="skip the measured MFMA / HBM-read ceilings")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the step: time every configuration of the parity tests, with the oracle's "
+                         "time on a sample of each, and print one JSON line with the table")
     ap.add_argument("--cpu-heads", type=int, default=8,
                     help="heads of batch 0 the CPU baseline computes (about 10-20 s)")
     args = ap.parse_args(argv)
@@ -333,6 +408,12 @@ def main(argv=None):
 
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration)
+    if args.configs:
+        from io_aware_tiled_fwd_amd import binding
+        binding.load_library()
+        table = config_table(oracle=not args.no_cpu_baseline)
+        print(json.dumps({"configs": table, "peak_bf16_tflops": PEAK_BF16_TFLOPS}), flush=True)
+        return 0
 
     import numpy as np
     import torch
