@@ -153,8 +153,11 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
     const int lq = lane & 31, h = lane >> 5;
     // Flat id -> (key/value head, key block): XCD-contiguous, head-major; key
     // blocks ascend, so for causal masks the heaviest blocks (the first ones,
-    // seen by the most queries) start first.  The G query heads sharing the
-    // key/value head (grouped heads) are walked one after the other, their
+    // seen by the most queries) start first.  Head-major keeps the workgroups
+    // that stream one head's Q and dO running together on one L2 (ordering
+    // the blocks heaviest-first across all of an XCD's heads measured 4-10%
+    // slower here).  The G query heads sharing the key/value
+    // head (grouped heads) are walked one after the other, their
     // contributions summed in the same accumulators.
     const int task = xcd_task(block_id(), BKV * nkb);
     if (task >= BKV * nkb) return;
@@ -667,11 +670,8 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
 
     const int tid = thread_id(), lane = tid & 63, w = wave_id();
     const int lq = lane & 31, h = lane >> 5;
-    const int task = xcd_task(block_id(), BH * nqb);
-    if (task >= BH * nqb) return;
-    const int bh = task / nqb;
-    const int qi = task % nqb;
-    const int qb = CAUSAL ? (nqb - 1 - qi) : qi;  // heaviest query blocks first
+    int bh, qb;
+    if (!wg_coords(block_id(), BH, nqb, CAUSAL, bh, qb)) return;  // heaviest query blocks first
     const int q0 = qb * kDqBq;
     const int qw0 = q0 + 32 * w;
     const int qrow = qw0 + lq;

@@ -97,14 +97,43 @@ __device__ __forceinline__ int xcd_task(int id, int total) {
     return (id % kNumXcd) * per + id / kNumXcd;
 }
 
-// Map a flat workgroup id to (head, query block): XCD-contiguous task ranges
-// (see xcd_task), head-major, and within a head the heaviest query block (the
-// last, under a causal mask) first.  Returns false for padding workgroups.
+// Map a flat workgroup id to (head, rank) for a grid of grid_for_tasks(nheads
+// * nranks) workgroups, rank 0 being a head's heaviest block.  When nheads is
+// a multiple of the XCD count, XCD x = id % 8 owns the contiguous heads
+// [x hp, (x + 1) hp), hp = nheads / 8, so that a head's K/V (and grouped
+// heads' shared K/V) stay in one L2.  The XCD's k-th workgroup (k = id / 8)
+// takes its heads in groups of g, g the largest divisor of hp with g nranks <=
+// 32 (the XCD's CUs), and walks a group rank-major: the heaviest blocks of its
+// g heads, then the next rank.  A group is about one round of the XCD's CUs,
+// so only g heads stream through the L2 at a time, and short causal grids no
+// longer end on one head's heaviest blocks (head-major order left B4 H16
+// N4096 17% above the ideal makespan).  Otherwise the XCDs receive contiguous
+// task ranges (xcd_task), head-major, heaviest rank first within a head.
+// Returns false for padding workgroups.
+constexpr int kCusPerXcd = 32;
+__device__ __forceinline__ bool head_rank(int id, int nheads, int nranks, int& head, int& rank) {
+    if (nheads % kNumXcd == 0) {
+        const int hp = nheads / kNumXcd, k = id / kNumXcd;
+        if (k >= hp * nranks) return false;
+        int g = max(1, min(hp, kCusPerXcd / nranks));
+        while (hp % g) --g;
+        const int gi = k / (g * nranks), r = k % (g * nranks);
+        rank = r / g;
+        head = (id % kNumXcd) * hp + gi * g + r % g;
+        return true;
+    }
+    const int task = xcd_task(id, nheads * nranks);
+    if (task >= nheads * nranks) return false;
+    head = task / nranks;
+    rank = task % nranks;
+    return true;
+}
+
+// (head, query block) of a forward or dQ workgroup: under a causal mask the
+// last query block is the heaviest.
 __device__ __forceinline__ bool wg_coords(int id, int BH, int nqb, bool causal, int& bh, int& qb) {
-    const int task = xcd_task(id, BH * nqb);
-    if (task >= BH * nqb) return false;
-    bh = task / nqb;
-    const int qi = task % nqb;
+    int qi;
+    if (!head_rank(id, BH, nqb, bh, qi)) return false;
     qb = causal ? (nqb - 1 - qi) : qi;
     return true;
 }
