@@ -379,14 +379,36 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
 //      phase 1  dV wavefront: S, P (masked), P -> LDS      dK wavefront: dP - D
 //      barrier
 //      phase 2  dV wavefront: dV^T += dO^T P              dK wavefront: dS, dK^T += Q^T dS
-//    P crosses in fp32 and every value is formed by the same operations in
-//    the same order as in the separate kernels, so the results are bitwise
-//    those of the dV and dK kernels.  With dropout the dV wavefront hands P
-//    with its sign bit set where the element is dropped; the dK wavefront
-//    needs no generator of its own.  (At d = 64 the separate kernels are
-//    faster and are used instead.)
+//    Without dropout the row statistics ride in the products: the staged Q
+//    and dO rows carry one more k-step, in their padding columns, holding
+//    -L/c and -D split exactly into three bf16 parts (fold_parts), and the
+//    wavefronts' register operands a matching k-step of ones, so the S chain
+//    yields S - L/c (P = 2^(c (S - L/c))) and the dP chain dP - D.  That costs
+//    one MFMA per eight and removes the per-row L and D values a lane would
+//    otherwise read from LDS as four 16-byte broadcasts per 32 queries each.
+//    With dropout (dS needs dP and D apart) L and D are read as in the
+//    separate kernels, P crosses in fp32 and every value is formed by the
+//    same operations in the same order as there, so the results are bitwise
+//    theirs; the dV wavefront hands P with its sign bit set where the element
+//    is dropped, and the dK wavefront needs no generator of its own.  (At
+//    d = 64 the separate kernels are faster and are used instead.)
 constexpr int kPairs = kBwdWaves / 2;
 constexpr int kFusedBkv = 32 * kPairs;  // keys per workgroup
+
+// x as hi + mid + lo, three bf16 values whose sum is x exactly (x finite:
+// each part takes the next 8 significant bits, and the residuals are exact
+// in fp32), packed as the 8 elements {hi, mid, lo, 0, 0, 0, 0, 0}.  -inf
+// (a row past N: P = 0) becomes {-inf, 0, 0, ...}.
+__device__ __forceinline__ u32x4 fold_parts(float x) {
+    bf16 hi = (bf16)x, mid = (bf16)0.f, lo = (bf16)0.f;
+    if (x != -INFINITY) {
+        const float r1 = x - (float)hi;
+        mid = (bf16)r1;
+        lo = (bf16)(r1 - (float)mid);
+    }
+    const bf16x8 v = {hi, mid, lo, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+    return __builtin_bit_cast(u32x4, v);
+}
 
 template <int D, bool CAUSAL, bool GROUPED, bool DROPOUT, typename OutT>
 __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_kernel(
@@ -400,10 +422,13 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
     constexpr int BQ = kDkvBq;
     constexpr int NQH = BQ / 32;
     constexpr int RS = both_ways_stride<D>();
+    constexpr bool FOLD = !DROPOUT;  // L and D ride in the products
+    constexpr int NKS = D / 16 + (FOLD ? 1 : 0);  // k-steps of the S and dP chains
+    static_assert(!FOLD || RS >= D + 16, "the folded k-step lives in the row padding");
     __shared__ __attribute__((aligned(16))) bf16 sQ[2][BQ * RS];
     __shared__ __attribute__((aligned(16))) bf16 sdO[2][BQ * RS];
-    __shared__ __attribute__((aligned(16))) float sL[2][BQ];
-    __shared__ __attribute__((aligned(16))) float sD[2][BQ];
+    __shared__ __attribute__((aligned(16))) float sL[FOLD ? 1 : 2][BQ];
+    __shared__ __attribute__((aligned(16))) float sD[FOLD ? 1 : 2][BQ];
     // P of pair p, sub-block qh, register group r, lane: one float4 per lane.
     __shared__ __attribute__((aligned(16))) f32x4 sP[kPairs][NQH][4][64];
     __shared__ __attribute__((aligned(16))) uint32_t sKeep[DROPOUT ? kPairs : 1][32];
@@ -426,8 +451,14 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
     const int qh0 = (kvh / (Hq / G)) * Hq + (kvh % (Hq / G)) * G;
     const uint32_t head_bytes = (uint32_t)N * D * 2;
 
-    // K^T (dV wavefront) or V^T (dK wavefront) operands of this lane's key.
-    bf16x8 kvf[D / 16];
+    // K^T (dV wavefront) or V^T (dK wavefront) operands of this lane's key;
+    // with FOLD a last k-step of ones (lane half 0: elements 0..2) meets the
+    // parts of -L/c or -D in the staged rows.
+    bf16x8 kvf[NKS];
+    if constexpr (FOLD) {
+        const bf16 one = h == 0 ? (bf16)1.f : (bf16)0.f, z = (bf16)0.f;
+        kvf[D / 16] = bf16x8{one, one, one, z, z, z, z, z};
+    }
     {
         const __amdgpu_buffer_rsrc_t rs = make_rsrc((dvw ? K : V) + base, head_bytes);
 #pragma unroll
@@ -473,10 +504,26 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
             stq.store(sQ[buf], RS);
             stg.store(sdO[buf], RS);
             if (tid < BQ) {
-                sL[buf][tid] = lreg;
-                sD[buf][tid] = dreg;
+                if constexpr (FOLD) {
+                    // Columns D .. D+7 of the row: the parts of -L/c and -D
+                    // (lreg = +inf past N gives -inf: P = 0).
+                    *reinterpret_cast<u32x4*>(&sQ[buf][tid * RS + D]) = fold_parts(-lreg / scale_log2);
+                    *reinterpret_cast<u32x4*>(&sdO[buf][tid * RS + D]) = fold_parts(-dreg);
+                } else {
+                    sL[buf][tid] = lreg;
+                    sD[buf][tid] = dreg;
+                }
             }
         };
+        if constexpr (FOLD) {
+            // Columns D+8 .. D+15 (the folded k-step of lane half 1) stay zero;
+            // the tile stores never touch them.
+            if (tid < 4 * BQ) {
+                const int t = tid % BQ, b = (tid / BQ) & 1;
+                bf16* dst = (tid / BQ) < 2 ? sQ[b] : sdO[b];
+                *reinterpret_cast<u32x4*>(&dst[t * RS + D + 8]) = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
         if (iq0 < nqblk) {
             load_block(iq0);
             store_block(0);
@@ -497,7 +544,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
             bf16x8 bop[2 * NQH];
             if (active) {
                 const bf16* src = dvw ? qt : gt;
-                constexpr int NR = NQH * (D / 16), AHEAD = 4;
+                constexpr int NR = NQH * NKS, AHEAD = 4;
                 auto rread = [&](int r) {
                     return lds_read16_early(src + 32 * (r % NQH) * RS + row_off + 16 * (r / NQH));
                 };
@@ -516,8 +563,9 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                 }
                 if (dvw) __builtin_amdgcn_s_setprio(0);
                 // The dK wavefront forms dP - D while its partner computes P,
-                // leaving one product per element for phase 2.
-                if constexpr (!DROPOUT) {
+                // leaving one product per element for phase 2 (with FOLD the
+                // chain has formed it).
+                if constexpr (!DROPOUT && !FOLD) {
                     if (!dvw) {
 #pragma unroll
                         for (int qh = 0; qh < NQH; ++qh)
@@ -553,12 +601,14 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                         float v[16];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[buf][32 * qh + 8 * r + 4 * h]);
+                            f32x4 l4 = f32x4{};
+                            if constexpr (!FOLD) l4 = *reinterpret_cast<const f32x4*>(&sL[buf][32 * qh + 8 * r + 4 * h]);
                             f32x4 hand;
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const int i = 4 * r + e;
-                                float p = fast_exp2(fmaf(t[qh][i], scale_log2, -l4[e]));
+                                float p = FOLD ? fast_exp2(t[qh][i] * scale_log2)
+                                               : fast_exp2(fmaf(t[qh][i], scale_log2, -l4[e]));
                                 if constexpr (MASK) {
                                     if (key > i0 + 32 * qh + c_row(i, h)) p = 0.f;
                                 }
@@ -924,9 +974,12 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const fl
     auto K = static_cast<const bf16*>(k);
     auto V = static_cast<const bf16*>(v);
     auto G = static_cast<const bf16*>(dout);
-    if (d == 64) {
-        // At d = 64 the separate kernels are faster: their steps are too short
-        // for the paired kernel's hand-over to pay.
+    // At d = 64 the separate kernels are faster: their steps are too short
+    // for the paired kernel's hand-over to pay.  Below |scale| = 2^-100 the
+    // paired kernel's folded -L/c (L < 2^5 there) could leave the fp32 range,
+    // so such calls take the separate kernels too (scale 0 folds exactly).
+    const bool tiny = scale != 0.f && fabsf(scale) < 0x1p-100f;
+    if (d == 64 || (tiny && !dropout)) {
         hipError_t e = launch_bwd_dv(q, k, lse, dout, dv, B, Hq, Hkv, N, d, scale, causal, dropout, grad_bf16, stream);
         if (e != hipSuccess) return e;
         return launch_bwd_dk(q, k, v, lse, dout, delta, dk, B, Hq, Hkv, N, d, scale, causal, dropout, grad_bf16,

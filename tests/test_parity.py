@@ -113,10 +113,10 @@ def test_c3_causal_bwd_bench_shape_sampled_heads():
     """The benchmark's step at its full size (B2 H32 N8192 d128, causal, the same
     seeded inputs): the backward through fa_bwd (preprocess, the paired dK/dV
     kernel, dQ), every gradient of four sampled heads against the oracle; on
-    every head the paired kernel's dK and dV equal, bitwise, those of the two
-    one-gradient kernels (fa_bwd_dk, fa_bwd_dv), which compute P themselves, so
-    a P hand-over error on any head would show; and the column-sum
-    invariants."""
+    every head the paired kernel's dK and dV agree with those of the two
+    one-gradient kernels (fa_bwd_dk, fa_bwd_dv), which compute P themselves, to
+    within rounding (_paired_close), so a P hand-over error on any head would
+    show; and the column-sum invariants."""
     w = inputs.WORKLOADS["c3_bf16_causal_n8192_d128"]
     B, H, N, d = w["B"], w["H"], w["N"], w["d"]
     ts = inputs.normal_qkv(B, H, N, d, w["seed"], with_dout=True)
@@ -133,7 +133,8 @@ def test_c3_causal_bwd_bench_shape_sampled_heads():
     binding.fa_bwd_dk(dev["q"], dev["k"], dev["v"], lse, dev["do"], delta, sk, True, scale)
     binding.fa_bwd_dv(dev["q"], dev["k"], lse, dev["do"], sv, True, scale)
     torch.cuda.synchronize()
-    assert torch.equal(sk, dk) and torch.equal(sv, dv), "paired dK/dV kernel differs from the one-gradient kernels"
+    _paired_close(sk, dk, "c3 dk")
+    _paired_close(sv, dv, "c3 dv")
     del sk, sv
     heads = inputs.sample_heads(B * H, 4, w["seed"] + 2000)
     arr = {n: ts.f64[n].reshape(B * H, N, d) for n in ("q", "k", "v", "do")}
@@ -363,13 +364,30 @@ def test_abi_errors_leave_outputs_untouched():
                        q[:, :, :, :96].contiguous(), o[:, :, :, :96].contiguous(), lse)
 
 
+def _paired_close(a, b, what):
+    """The one-gradient kernels' dK or dV (a) against the paired kernel's (b) at
+    d = 128.  Without dropout the paired kernel folds L and D into its score
+    and dP products (an exact three-part bf16 split of -L/c and -D against a
+    k-step of ones) where the one-gradient kernels subtract them after the
+    product, so P and dP - D differ by a few fp32 roundings and a P element
+    may round to the neighbouring bf16 value: the gradients agree to well
+    under 1e-3 of their largest magnitude, while a P handed to the wrong lane
+    or row would move them by O(1) of it."""
+    e = (a - b).abs().max().item()
+    m = b.abs().max().item()
+    _say(f"{what}: one-gradient vs paired max|diff|={e:.3e} (max|x|={m:.3e})")
+    assert e <= 1e-3 * m, f"{what}: paired kernel differs from the one-gradient kernels by {e} (max {m})"
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_backward_stages_equal_fa_bwd(d):
     """fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq in stream order are fa_bwd; the
-    one-gradient kernels (fa_bwd_dv, fa_bwd_dk) give the same dV and dK bitwise.
-    At d = 128 fa_bwd_dkdv is the paired-wavefront kernel, so this also checks
-    that P handed from one wavefront to its partner arrives intact, over
-    several key blocks, causal diagonal blocks and a ragged tail."""
+    one-gradient kernels (fa_bwd_dv, fa_bwd_dk) give the same dV and dK,
+    bitwise at d = 64 (where fa_bwd runs them) and to within rounding at
+    d = 128 (_paired_close), where fa_bwd_dkdv is the paired-wavefront kernel,
+    so this also checks that P handed from one wavefront to its partner
+    arrives intact, over several key blocks, causal diagonal blocks and a
+    ragged tail."""
     for causal in (False, True):
         ts = inputs.normal_qkv(1, 3, 777, d, 71, with_dout=True)
         dev = upload(ts)
@@ -383,5 +401,10 @@ def test_backward_stages_equal_fa_bwd(d):
         binding.fa_bwd_dv(dev["q"], dev["k"], lse, dev["do"], ov, causal)
         binding.fa_bwd_dk(dev["q"], dev["k"], dev["v"], lse, dev["do"], delta, ok, causal)
         torch.cuda.synchronize()
-        for a, b in ((sq, dq), (sk, dk), (sv, dv), (ok, dk), (ov, dv)):
+        for a, b in ((sq, dq), (sk, dk), (sv, dv)):
             assert torch.equal(a, b)
+        if d == 64:
+            assert torch.equal(ok, dk) and torch.equal(ov, dv)
+        else:
+            _paired_close(ok, dk, f"d128 causal={causal} dk")
+            _paired_close(ov, dv, f"d128 causal={causal} dv")

@@ -90,8 +90,12 @@ def test_dropout_causal_n8192_sampled_rows():
 
 
 def test_dropout_p0_equals_plain_path_and_seeds_matter():
-    """p = 0 drops nothing: bitwise the plain forward and backward.  The same
-    seed and offset reproduce bitwise; another offset changes the output."""
+    """p = 0 drops nothing: bitwise the plain forward and dQ; dK and dV to
+    within rounding, since without dropout the paired dK/dV kernel folds L
+    and D into its products while the dropout variant subtracts them after
+    (the one-gradient comparison in test_parity.py states the bound).  The
+    same seed and offset reproduce bitwise; another offset changes the
+    output."""
     B, Hq, Hkv, N, d = 1, 4, 2, 500, 128
     ts = inputs.normal_gqa(B, Hq, Hkv, N, d, 20303, with_dout=True)
     scale = inputs.default_scale(d)
@@ -100,8 +104,9 @@ def test_dropout_p0_equals_plain_path_and_seeds_matter():
     g = binding.attention_bwd(dev["q"], dev["k"], dev["v"], o, lse, dev["do"], causal=True, scale=scale)
     torch.cuda.synchronize()
     assert torch.equal(o0, o) and torch.equal(l0, lse)
-    for a, b in zip(g0, g):
-        assert torch.equal(a, b)
+    assert torch.equal(g0[0], g[0])  # dQ
+    for a, b in zip(g0[1:], g[1:]):  # dK, dV
+        assert (a - b).abs().max().item() <= 1e-3 * b.abs().max().item()
     _, o1, _, g1 = _run(ts, 0.3, True, scale, offset=1)
     _, o2, _, g2 = _run(ts, 0.3, True, scale, offset=1)
     _, o3, _, _ = _run(ts, 0.3, True, scale, offset=2)

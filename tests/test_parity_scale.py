@@ -44,12 +44,15 @@ def _grad_bar(scale, d):
 @pytest.mark.parametrize("causal", [False, True])
 def test_bf16_fwd_bwd_any_scale(d, causal):
     """bf16 forward and backward (every stage, both dK/dV kernels at d = 128
-    through fa_bwd) at negative, zero and positive scales, ragged N = 300."""
+    through fa_bwd) at negative, zero and positive scales, ragged N = 300;
+    also at 2^-90, where the paired dK/dV kernel still folds -L/c (about
+    2^94) into its products, and at -1e-35, below 2^-100, where fa_bwd takes
+    the separate dK and dV kernels instead."""
     N = 300
     ts = inputs.normal_qkv(1, 2, N, d, 1300 + d, with_dout=True)
     dev = upload(ts)
     arr = [ts.f64[n].reshape(2, N, d) for n in ("q", "k", "v", "do")]
-    for scale in _scales(d):
+    for scale in _scales(d) + [2.0 ** -90, -1e-35]:
         what = f"bf16 d={d} causal={causal} scale={scale}"
         _say(what)
         o, lse = binding.attention_fwd(dev["q"], dev["k"], dev["v"], causal=causal, scale=scale)
