@@ -29,6 +29,8 @@
 // Latency: the K fragments of S are read four MFMAs ahead, and the V^T
 // fragments of the first two k-steps of O^T are read right after S, so that
 // the exponentials of the softmax run while they arrive.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -133,16 +135,21 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     load_tile(0);
     store_tile(0);
     __syncthreads();
-    for (int j = 0; j < ntiles; ++j) {
+    // One key tile.  MASKED tiles may cross a wave's diagonal or the ragged
+    // end; the others carry no masking code at all, so no branch splits their
+    // loop body and the compiler schedules the scores, the softmax and P V
+    // as one block (with the masking branch merely present, never taken, the
+    // d = 64 forward ran 21% slower).
+    auto step = [&](int j, auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mask_tag)::value;
         const int buf = j & 1;
         load_tile(min(j + 1, ntiles - 1));  // in flight during this tile's math
 
         const int k0 = j * BC;
         // Skip tiles entirely above this wave's diagonal (a scalar branch).
-        if (!CAUSAL || __builtin_amdgcn_readfirstlane(k0 <= qw0 + 31)) {
+        if (!CAUSAL || !MASKED || __builtin_amdgcn_readfirstlane(k0 <= qw0 + 31)) {
             const bf16* kt = sK[buf];
             const bf16* vt = sV[buf];
-            if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
             // S^T = K Q^T for two 32-key halves, the two accumulation chains interleaved.
             f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -160,7 +167,6 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
 
             bf16x8 vpre[NPRE][NDB];
 #pragma unroll
@@ -169,7 +175,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
                 for (int db = 0; db < NDB; ++db) vpre[s2][db] = lds_read_tr_a(vt + 16 * s2 * VS + v_off + 32 * db, VS);
 
             // Mask keys past N and, on tiles crossing the diagonal, keys after the query.
-            if (k0 + BC > N || (CAUSAL && k0 + BC - 1 > qw0)) {
+            if (MASKED && (k0 + BC > N || (CAUSAL && k0 + BC - 1 > qw0))) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -213,7 +219,6 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
             l += rs0 + rs1;
 
             // O^T += V^T P^T, k-step by k-step.
-            if constexpr (D == 64) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int s2 = 0; s2 < BC / 16; ++s2)
 #pragma unroll
@@ -222,12 +227,15 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
                                                 : lds_read_tr_a(vt + 16 * s2 * VS + v_off + 32 * db, VS);
                     oacc[db] = mfma_bf16_32x32x16(vf, pf[s2], oacc[db]);
                 }
-            if constexpr (D == 64) __builtin_amdgcn_s_setprio(0);
         }
 
         store_tile(buf ^ 1);  // buffers last read in the previous tile
         __syncthreads();
-    }
+    };
+    // Tiles before j_split are wholly visible to every wave of the workgroup.
+    const int j_split = CAUSAL ? min(ntiles, q0 / BC) : (N % BC ? ntiles - 1 : ntiles);
+    for (int j = 0; j < j_split; ++j) step(j, std::false_type{});
+    for (int j = j_split; j < ntiles; ++j) step(j, std::true_type{});
 
     // Epilogue: O = acc / l, L = (m + log2 l) ln 2.
     const float lt = pair_sum(l);

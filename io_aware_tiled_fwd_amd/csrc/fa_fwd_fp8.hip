@@ -28,6 +28,8 @@
 //    64 ks + 32 h .. +31, P^T and V^T at the key slots described below;
 //  - V^T is produced with identity MFMAs in fp8 (exact: x * 1 and x * 0),
 //    written back as e4m3 (exact, the values came from e4m3).
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -170,12 +172,15 @@ __global__ __launch_bounds__(kF8Threads, 1) void fwd_fp8_kernel(
     load_tile(0);
     store_tile(0);
     __syncthreads();
-    for (int j = 0; j < ntiles; ++j) {
+    // One key tile; MASKED tiles may cross a wave's diagonal or the ragged
+    // end, the others carry no masking code (no branch splits their body).
+    auto step = [&](int j, auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(mask_tag)::value;
         const int buf = j & 1;
         load_tile(min(j + 1, ntiles - 1));  // in flight during this tile's math
 
         const int k0 = j * BC;
-        if (!CAUSAL || __builtin_amdgcn_readfirstlane(k0 <= qw0 + 31)) {
+        if (!CAUSAL || !MASKED || __builtin_amdgcn_readfirstlane(k0 <= qw0 + 31)) {
             const uint8_t* kt = sK[buf];
             const uint8_t* vt = sVt[buf];
             f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(kF8Threads, 1) void fwd_fp8_kernel(
 #pragma unroll
             for (int db = 0; db < NDB; ++db) vf[db] = lds_read32(vt + 32 * db * VTS + v_off);
 
-            if (k0 + BC > N || (CAUSAL && k0 + BC - 1 > qw0)) {
+            if (MASKED && (k0 + BC > N || (CAUSAL && k0 + BC - 1 > qw0))) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -234,7 +239,11 @@ __global__ __launch_bounds__(kF8Threads, 1) void fwd_fp8_kernel(
 
         store_tile(buf ^ 1);
         __syncthreads();
-    }
+    };
+    // Tiles before j_split are wholly visible to every wave of the workgroup.
+    const int j_split = CAUSAL ? min(ntiles, q0 / BC) : (N % BC ? ntiles - 1 : ntiles);
+    for (int j = 0; j < j_split; ++j) step(j, std::false_type{});
+    for (int j = j_split; j < ntiles; ++j) step(j, std::true_type{});
 
     const float lt = pair_sum(l);
     if (qrow < N) {
