@@ -484,7 +484,11 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
     const int row_off = lq * RS + 8 * h;
     const int tr_off = tr_row(lane) * RS + tr_col(lane);
 
-    auto run_head = [&](int qh_idx) {
+    // Each role runs the loop as its own copy (DVW fixed at compile time), so
+    // no role test branches inside a step and splits its scheduling regions;
+    // both copies pass the same barriers.
+    auto run_head = [&](int qh_idx, auto role_tag) __attribute__((always_inline)) {
+        constexpr bool DVW = decltype(role_tag)::value;
         const int64_t qbase = (int64_t)qh_idx * N;
         const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + qbase * D, head_bytes);
         const __amdgpu_buffer_rsrc_t grs = make_rsrc(dO + qbase * D, head_bytes);
@@ -529,7 +533,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
             store_block(0);
         }
         __syncthreads();
-        auto step = [&](int iq, auto mask_tag) {
+        auto step = [&](int iq, auto mask_tag) __attribute__((always_inline)) {
             constexpr bool MASK = decltype(mask_tag)::value;
             const int buf = (iq - iq0) & 1;
             load_block(min(iq + 1, nqblk - 1));
@@ -543,7 +547,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
             f32x16 t[NQH];
             bf16x8 bop[2 * NQH];
             if (active) {
-                const bf16* src = dvw ? qt : gt;
+                const bf16* src = DVW ? qt : gt;
                 constexpr int NR = NQH * NKS, AHEAD = 4;
                 auto rread = [&](int r) {
                     return lds_read16_early(src + 32 * (r % NQH) * RS + row_off + 16 * (r / NQH));
@@ -553,20 +557,16 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                 for (int r = 0; r < AHEAD; ++r) ra[r] = rread(r);
 #pragma unroll
                 for (int qh = 0; qh < NQH; ++qh) t[qh] = f32x16{};
-                // The S chain at raised priority: the partner's dP chain fills
-                // the MFMA unit while this wavefront computes P.
-                if (dvw) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
                 for (int r = 0; r < NR; ++r) {
                     if (r + AHEAD < NR) ra[r + AHEAD] = rread(r + AHEAD);
                     t[r % NQH] = mfma_bf16_32x32x16(ra[r], kvf[r / NQH], t[r % NQH]);
                 }
-                if (dvw) __builtin_amdgcn_s_setprio(0);
                 // The dK wavefront forms dP - D while its partner computes P,
                 // leaving one product per element for phase 2 (with FOLD the
                 // chain has formed it).
-                if constexpr (!DROPOUT && !FOLD) {
-                    if (!dvw) {
+                if constexpr (!DROPOUT && !FOLD && !DVW) {
+                    {
 #pragma unroll
                         for (int qh = 0; qh < NQH; ++qh)
 #pragma unroll
@@ -577,7 +577,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                             }
                     }
                 }
-                if (dvw) {
+                if constexpr (DVW) {
 #pragma unroll
                     for (int qh = 0; qh < NQH; ++qh) {
                         uint32_t keep_bits[4];  // bit lq of word e of group r: query 32 qh + 8 r + 4 h + e kept
@@ -631,8 +631,8 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
             __syncthreads();  // P of every pair is in LDS
             // Phase 2: the gradient products.
             if (active) {
-                const bf16* at = dvw ? gt : qt;
-                if (!dvw) {
+                const bf16* at = DVW ? gt : qt;
+                if constexpr (!DVW) {
 #pragma unroll
                     for (int qh = 0; qh < NQH; ++qh) {
                         float v[16];
@@ -676,7 +676,11 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
         for (int iq = iq0; iq < iq_split; ++iq) step(iq, std::true_type{});
         for (int iq = max(iq0, iq_split); iq < nqblk; ++iq) step(iq, std::false_type{});
     };
-    for (int g = 0; g < G; ++g) run_head(qh0 + g);
+    if (dvw) {
+        for (int g = 0; g < G; ++g) run_head(qh0 + g, std::true_type{});
+    } else {
+        for (int g = 0; g < G; ++g) run_head(qh0 + g, std::false_type{});
+    }
 
     if (key < N) {
         OutT* op = (dvw ? dVout : dKout) + base + (int64_t)key * D + 4 * h;
