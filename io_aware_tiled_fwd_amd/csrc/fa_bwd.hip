@@ -376,10 +376,13 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
 //    computed once for both gradients (8 products per tile instead of the
 //    separate kernels' 10) while each wavefront still holds a single fp32
 //    accumulator, so two wavefronts share each SIMD as before.  Per 64-query
-//    step:
-//      phase 1  dV wavefront: S, P (masked), P -> LDS      dK wavefront: dP - D
+//    step n:
+//      phase 1  dV wavefront: S, P (masked), P -> LDS      dK wavefront: dP - D, then
+//                                                          dK^T += Q^T dS of step n-1
 //      barrier
-//      phase 2  dV wavefront: dV^T += dO^T P              dK wavefront: dS, dK^T += Q^T dS
+//      phase 2  dV wavefront: dV^T += dO^T P              dK wavefront: dS of step n
+//    so each wavefront's VALU work (softmax; dS) runs beside its partner's
+//    MFMAs; the last step's dK products follow the loop.
 //    Without dropout the row statistics ride in the products: the staged Q
 //    and dO rows carry one more k-step, in their padding columns, holding
 //    -L/c and -D split exactly into three bf16 parts (fold_parts), and the
@@ -534,6 +537,27 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
             store_block(0);
         }
         __syncthreads();
+        // The dK wavefront defers its dK MFMAs by one step: dS of step n is
+        // formed in phase 2 of step n (beside its partner's dV MFMAs) and its
+        // products are issued in phase 1 of step n + 1 (beside its partner's
+        // softmax), against step n's Q tile, which stays in the other buffer
+        // until step n + 1 stages over it at its end.
+        bf16x8 dsk[2 * NQH];
+        bool pend = false;      // wave-uniform: dsk holds an unissued step
+        const bf16* q_prev = sQ[0];
+        auto dk_products = [&](const bf16* qsrc) __attribute__((always_inline)) {
+#pragma unroll
+            for (int qh = 0; qh < NQH; ++qh) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(qsrc + 32 * qh * RS + tr_off + 32 * db, RS),
+                                                 dsk[2 * qh], acc[db]);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(qsrc + (32 * qh + 16) * RS + tr_off + 32 * db, RS),
+                                                 dsk[2 * qh + 1], acc[db]);
+            }
+        };
         auto step = [&](int iq, auto mask_tag) __attribute__((always_inline)) {
             constexpr bool MASK = decltype(mask_tag)::value;
             const int buf = (iq - iq0) & 1;
@@ -629,6 +653,9 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                     }
                 }
             }
+            if constexpr (!DVW) {
+                if (pend) dk_products(q_prev);
+            }
             __syncthreads();  // P of every pair is in LDS
             // Phase 2: the gradient products.
             if (active) {
@@ -653,12 +680,13 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                                 for (int e = 0; e < 4; ++e) v[4 * r + e] = got[e] * t[qh][4 * r + e];
                             }
                         }
-                        bop[2 * qh] = pack_bf16x8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
-                        bop[2 * qh + 1] = pack_bf16x8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
+                        dsk[2 * qh] = pack_bf16x8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+                        dsk[2 * qh + 1] = pack_bf16x8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
                     }
                 }
-                // A = Q^T (dK) or dO^T (dV): transposing reads; k-step s2 of
+                // dV wavefront: A = dO^T by transposing reads; k-step s2 of
                 // sub-block qh covers queries 32 qh + 16 s2 + {4h + e, 8 + 4h + e}.
+                if constexpr (DVW)
 #pragma unroll
                 for (int qh = 0; qh < NQH; ++qh) {
 #pragma unroll
@@ -671,11 +699,22 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                             lds_read_tr_a(at + (32 * qh + 16) * RS + tr_off + 32 * db, RS), bop[2 * qh + 1], acc[db]);
                 }
             }
+            if constexpr (!DVW) {
+                pend = active;
+                q_prev = qt;
+            }
             store_block(buf ^ 1);
             __syncthreads();
         };
         for (int iq = iq0; iq < iq_split; ++iq) step(iq, std::true_type{});
         for (int iq = max(iq0, iq_split); iq < nqblk; ++iq) step(iq, std::false_type{});
+        // The last step's products: its Q tile is intact (the last staging
+        // store went to the other buffer).
+        if constexpr (!DVW) {
+            if (pend) dk_products(q_prev);
+        }
+        // Grouped heads: the next head's prologue stages into buffer 0.
+        if constexpr (GROUPED) __syncthreads();
     };
     if (dvw) {
         for (int g = 0; g < G; ++g) run_head(qh0 + g, std::true_type{});
