@@ -832,12 +832,23 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
 #pragma unroll
             for (int kh = 0; kh < BKV / 32; ++kh) {
                 f32x16 s = f32x16{}, dp = f32x16{};
+                // Row fragments requested AHEAD MFMAs before their use (even r:
+                // K rows for S^T, odd r: V rows for dP^T); the compiler's own
+                // order read them one or two MFMAs ahead and waited before most
+                // MFMAs (non-causal N18000 4% slower, causal within 1%).
+                constexpr int NR = 2 * (D / 16), AHEAD = 4;
+                auto rread = [&](int r) {
+                    return (r & 1) ? lds_read16_early(vt + 32 * kh * VS + v_off + 16 * (r >> 1))
+                                   : lds_read16_early(kt + 32 * kh * KS + k_off + 16 * (r >> 1));
+                };
+                bf16x8 ra[NR];
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    s = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(kt + 32 * kh * KS + k_off + 16 * ks),
-                                           qf[ks], s);
-                    dp = mfma_bf16_32x32x16(*reinterpret_cast<const bf16x8*>(vt + 32 * kh * VS + v_off + 16 * ks),
-                                            gf[ks], dp);
+                for (int r = 0; r < AHEAD; ++r) ra[r] = rread(r);
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    if (r + AHEAD < NR) ra[r + AHEAD] = rread(r + AHEAD);
+                    if (r & 1) dp = mfma_bf16_32x32x16(ra[r], gf[r >> 1], dp);
+                    else s = mfma_bf16_32x32x16(ra[r], qf[r >> 1], s);
                 }
                 float v[16];
                 u32x4 dw;
