@@ -657,9 +657,9 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                 if (pend) dk_products(q_prev);
             }
             __syncthreads();  // P of every pair is in LDS
-            // Phase 2: the gradient products.
+            // Phase 2: dS (dK wavefront; its products follow in the next
+            // step) and the dV products.
             if (active) {
-                const bf16* at = DVW ? gt : qt;
                 if constexpr (!DVW) {
 #pragma unroll
                     for (int qh = 0; qh < NQH; ++qh) {
@@ -686,17 +686,19 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                 }
                 // dV wavefront: A = dO^T by transposing reads; k-step s2 of
                 // sub-block qh covers queries 32 qh + 16 s2 + {4h + e, 8 + 4h + e}.
-                if constexpr (DVW)
+                if constexpr (DVW) {
 #pragma unroll
-                for (int qh = 0; qh < NQH; ++qh) {
+                    for (int qh = 0; qh < NQH; ++qh) {
 #pragma unroll
-                    for (int db = 0; db < D / 32; ++db)
-                        acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(at + 32 * qh * RS + tr_off + 32 * db, RS),
-                                                     bop[2 * qh], acc[db]);
+                        for (int db = 0; db < D / 32; ++db)
+                            acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(gt + 32 * qh * RS + tr_off + 32 * db, RS),
+                                                         bop[2 * qh], acc[db]);
 #pragma unroll
-                    for (int db = 0; db < D / 32; ++db)
-                        acc[db] = mfma_bf16_32x32x16(
-                            lds_read_tr_a(at + (32 * qh + 16) * RS + tr_off + 32 * db, RS), bop[2 * qh + 1], acc[db]);
+                        for (int db = 0; db < D / 32; ++db)
+                            acc[db] = mfma_bf16_32x32x16(
+                                lds_read_tr_a(gt + (32 * qh + 16) * RS + tr_off + 32 * db, RS), bop[2 * qh + 1],
+                                acc[db]);
+                    }
                 }
             }
             if constexpr (!DVW) {
