@@ -101,11 +101,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     int ntiles = (N + BC - 1) / BC;
     if (CAUSAL) ntiles = min(ntiles, (min(q0 + kFwdBr, N) - 1) / BC + 1);
 
-    // Staging of tile j+1 through registers.  K: thread chunk r covers row
-    // (tid + 512 r) / DCH, 16-byte column tid % DCH.  V: the tile is cut into
-    // half-blocks of 32 keys x 16 dimensions, HB consecutive ones per wave; a
-    // lane loads V[32 vkb + lq][16 vd16 + 8 h .. +7] of each, the MFMA operand
-    // A of C = V I.  Tile offsets ride in the scalar offset.
+    // Staging of tile j+1 through registers, K and V alike as row-major
+    // copies: thread chunk r covers row (tid + 512 r) / DCH, 16-byte column
+    // tid % DCH.  Tile offsets ride in the scalar offset.
     constexpr int ROWS_PER_PASS = kFwdThreads / DCH;
     const int ld_off = ((tid / DCH) * D + 8 * (tid % DCH)) * 2;
     u32x4 kreg[CH], vreg[CH];
