@@ -285,7 +285,7 @@ def probe_leg(mfma_blocks=1024, mfma_iters=2000, read_mib=1024, reps=3):
                    f"{nbytes >> 20} MiB read once with 16-byte non-temporal loads (fa_probe.h)"}
 
 
-def config_table(iters=20, warmup=5, oracle=True):
+def config_table(iters=30, warmup=10, oracle=True):
     """Every workload of the parity tests (inputs.WORKLOADS: the five configurations),
     each on its own seeded inputs: GPU time of the forward (and of the backward
     where the workload has one, plus the causal B2 H32 N8192 backward), the
