@@ -82,14 +82,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_base, head_bytes);
 
     // Q^T operand: k-step ks holds Q[qrow][16 ks + 8 h .. +7], carrying the
-    // sign of the scale (ScoreScale).
+    // sign of the scale (ScoreScale) once loaded (below, after the first
+    // tile's loads are issued too).
     bf16x8 qf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
         qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(qrs, (lq * D + 16 * ks + 8 * h) * 2, qw0 * D * 2));
-    wait_vmem_loads();
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = apply_sign(qf[ks], ss);
 
     f32x16 oacc[NDB];
 #pragma unroll
@@ -130,7 +128,12 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     // Loads and stores are unconditional (the last iteration re-reads the final
     // tile into the idle buffer): every path then drains the load counter at the
     // store, so the compiler never makes the math wait on a pending load.
+    // Q's loads and the first tile's share one memory round trip; the one
+    // wait for both keeps the compiler from guarding Q's uses in the loop.
     load_tile(0);
+    wait_vmem_loads();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = apply_sign(qf[ks], ss);
     store_tile(0);
     __syncthreads();
     // One key tile.  MASKED tiles may cross a wave's diagonal or the ragged
