@@ -28,11 +28,26 @@
 //
 // Latency: the K fragments of S are read four MFMAs ahead, and the V^T
 // fragments of the first two k-steps of O^T are read right after S, so that
-// the exponentials of the softmax run while they arrive.
+// the exponentials of the softmax run while they arrive.  At d = 128 the
+// unmasked tiles run instead as a hand-scheduled loop (fa_fwd_asm.inc) that
+// issues the next tile's scores and this tile's P V between the softmax's
+// VALU instructions.
+//
+// The grid is persistent: as many workgroups as fit on the GPU at once, each
+// taking its XCD's (head, query block) tasks in snake order.
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "fa_common.h"
+#include "fa_fwd_asm.inc"
 #include "fa_internal.h"
+
+// FA_FWD_ASM = 0 builds the forward without the hand-scheduled key loop
+// (every tile compiler-scheduled), for comparisons.
+#ifndef FA_FWD_ASM
+#define FA_FWD_ASM 1
+#endif
 
 namespace fa {
 
@@ -43,6 +58,25 @@ constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr int kFwdBr = 32 * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBc = 64;              // keys per tile
 
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x32 __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+// Byte address in LDS of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// The four words of the buffer resource that make_rsrc builds, as SGPR
+// operands of inline assembly.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    return u32x4{lo, hi & 0xFFFFu, n, 0x00020000u};
+}
+
 // DROPOUT: P V uses P with the dropped elements zeroed (the dropout mask of
 // fa_common.h); l and L stay those of the undropped P, and O carries the keep
 // scale.
@@ -50,7 +84,7 @@ template <int D, bool CAUSAL, bool DROPOUT>
 __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int N, int BH, int nqb, ScoreScale ss, int Hq, int G,
-    DropoutParams dp) {
+    DropoutParams dp, int nx) {
     const float scale_log2 = ss.c;
     constexpr int BC = kFwdBc;
     constexpr int KS = D + 8;   // K row stride: 16 consecutive rows hit distinct banks (b128 reads)
@@ -65,13 +99,28 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     __shared__ __attribute__((aligned(16))) bf16 sK[2][BC * KS];
     __shared__ __attribute__((aligned(16))) bf16 sV[2][BC * VS];
 
-    const int tid = thread_id(), lane = tid & 63, w = wave_id();
-    const int lq = lane & 31, h = lane >> 5;
+    const int w = wave_id();
+    // Persistent workgroups: nx per XCD, at most one per CU.  Workgroup ci of
+    // XCD xi takes the XCD's tasks (wg_coords order: a head's query blocks
+    // together, heaviest first) in snake order -- ci, then 2 nx - 1 - ci, then
+    // 2 nx + ci, ... -- so that a heavy task and a light one alternate on every
+    // CU.  Launching one workgroup per task instead left CUs idle between
+    // tasks: workgroups are dealt to the XCDs in id order, so an XCD whose CUs
+    // are all busy holds back the dispatch of the workgroups behind it.
+    const int xi = block_id() % kNumXcd, ci = block_id() / kNumXcd;
+    for (int round = 0;; ++round) {
+    const int task = round * nx + ((round & 1) ? nx - 1 - ci : ci);
     int bh, qb;
-    if (!wg_coords(block_id(), BH, nqb, CAUSAL, bh, qb)) return;
+    if (!wg_coords(task * kNumXcd + xi, BH, nqb, CAUSAL, bh, qb)) break;
+    // The lane's offsets are recomputed for every task (the empty asm hides
+    // that they do not change): hoisted out of the task loop they would stay
+    // live across it and push the kernel past its register budget.
+    int tid = thread_id();
+    asm volatile("" : "+v"(tid));
+    int lane = tid & 63, lq = lane & 31, h = lane >> 5;
     const int q0 = qb * kFwdBr;
     const int qw0 = q0 + 32 * w;  // first query row of this wave
-    const int qrow = qw0 + lq;    // this lane's query row
+    int qrow = qw0 + lq;          // this lane's query row
     const int64_t base = (int64_t)bh * N * D;
     const int64_t kv_base = (int64_t)kv_head(bh, Hq, G) * N * D;  // grouped heads share K, V
 
@@ -89,12 +138,13 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     for (int ks = 0; ks < NKS; ++ks)
         qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(qrs, (lq * D + 16 * ks + 8 * h) * 2, qw0 * D * 2));
 
+    // Accumulators and the running statistics: set by the assembly loop, or
+    // to their initial values (O = 0, m = -inf, l = 0) before the first
+    // compiler-scheduled tile.
     f32x16 oacc[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-    float m = -INFINITY;  // reference maximum of the scaled (log2-domain) scores
-    float mneg = 0.f;     // -m, or 0 while m = -inf (a row with nothing visible yet)
-    float l = 0.f;        // running partial sum over this lane's keys
+    float m;     // reference maximum of the scaled (log2-domain) scores
+    float mneg;  // -m, or 0 while m = -inf (a row with nothing visible yet)
+    float l;     // running partial sum over this lane's keys
 
     int ntiles = (N + BC - 1) / BC;
     if (CAUSAL) ntiles = min(ntiles, (min(q0 + kFwdBr, N) - 1) / BC + 1);
@@ -103,7 +153,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     // copies: thread chunk r covers row (tid + 512 r) / DCH, 16-byte column
     // tid % DCH.  Tile offsets ride in the scalar offset.
     constexpr int ROWS_PER_PASS = kFwdThreads / DCH;
-    const int ld_off = ((tid / DCH) * D + 8 * (tid % DCH)) * 2;
+    int ld_off = ((tid / DCH) * D + 8 * (tid % DCH)) * 2;
     u32x4 kreg[CH], vreg[CH];
     auto load_tile = [&](int j) {
         const int soff = j * BC * D * 2;
@@ -122,20 +172,114 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     };
 
     // Per-lane offsets of the K rows and the V^T rows.
-    const int k_off = lq * KS + 8 * h;
-    const int v_off = tr_row(lane) * VS + tr_col(lane);
+    int k_off = lq * KS + 8 * h;
+    int v_off = tr_row(lane) * VS + tr_col(lane);
 
-    // Loads and stores are unconditional (the last iteration re-reads the final
-    // tile into the idle buffer): every path then drains the load counter at the
-    // store, so the compiler never makes the math wait on a pending load.
+    // Tiles before j_split are wholly visible to every wave of the workgroup.
+    const int j_split = CAUSAL ? min(ntiles, q0 / BC) : (N % BC ? ntiles - 1 : ntiles);
+
+    // The unmasked tiles of the d = 128 forward run as one hand-scheduled
+    // block of inline assembly (fa_fwd_asm.inc, written by gen_fwd_asm.py):
+    // the next tile's score MFMAs and the current tile's P V MFMAs are issued
+    // between the softmax's VALU instructions.  It stages K(0), V(0), K(1)
+    // from the registers loaded here, computes every unmasked tile, and
+    // leaves K(j_split), V(j_split) in LDS buffer j_split & 1 for the masked
+    // tiles below, as the compiler-scheduled steps expect.
+    constexpr bool kAsmLoop = FA_FWD_ASM && D == 128 && !DROPOUT;
+    const bool use_asm = kAsmLoop && j_split >= 1;
     // Q's loads and the first tile's share one memory round trip; the one
     // wait for both keeps the compiler from guarding Q's uses in the loop.
-    load_tile(0);
+    // Loads and stores of the compiler-scheduled steps are unconditional (the
+    // last step re-reads the final tile into the idle buffer): every path
+    // then drains the load counter at the store, so the compiler never makes
+    // the math wait on a pending load.
+    u32x8 kst, vst, k1st;  // the assembly loop's first tiles: K(0), V(0), K(1)
+    if (use_asm) {
+#pragma unroll
+        for (int r = 0; r < CH; ++r) {
+            const u32x4 k0r = buffer_load16(krs, ld_off + r * ROWS_PER_PASS * D * 2, 0);
+            const u32x4 v0r = buffer_load16(vrs, ld_off + r * ROWS_PER_PASS * D * 2, 0);
+            const u32x4 k1r = buffer_load16(krs, ld_off + r * ROWS_PER_PASS * D * 2, BC * D * 2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kst[4 * r + e] = k0r[e];
+                vst[4 * r + e] = v0r[e];
+                k1st[4 * r + e] = k1r[e];
+            }
+        }
+    } else {
+        load_tile(0);
+    }
     wait_vmem_loads();
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = apply_sign(qf[ks], ss);
-    store_tile(0);
-    __syncthreads();
+    if (use_asm) {
+        if constexpr (kAsmLoop) {
+            u32x32 qall;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const u32x4 w4 = __builtin_bit_cast(u32x4, qf[ks]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qall[4 * ks + e] = w4[e];
+            }
+            const u32x4 krw = rsrc_words(K + kv_base, head_bytes);
+            const u32x4 vrw = rsrc_words(V + kv_base, head_bytes);
+            const uint32_t kaddr = lds_addr(sK[0] + k_off), vaddr = lds_addr(sV[0] + v_off);
+            const uint32_t kw = lds_addr(sK[0] + (tid / DCH) * KS + 8 * (tid % DCH));
+            const uint32_t vw = lds_addr(sV[0] + (tid / DCH) * VS + 8 * (tid % DCH));
+            const uint32_t ld0 = ld_off, ld1 = ld_off + ROWS_PER_PASS * D * 2;
+            f32x32 olo, ohi;
+            float m_out, mneg_out, l_out;
+            int cnt = j_split - 1, soffk, soffv;
+            asm volatile(FA_FWD128_ASM
+                         : [olo] "=" FA_FWD128_C_OLO(olo), [ohi] "=" FA_FWD128_C_OHI(ohi),
+                           [kst] "+" FA_FWD128_C_KST(kst), [vst] "+" FA_FWD128_C_VST(vst),
+                           [k1st] "+" FA_FWD128_C_K1ST(k1st), [m] "=" FA_FWD128_C_M(m_out),
+                           [mneg] "=" FA_FWD128_C_MNEG(mneg_out), [l] "=" FA_FWD128_C_L(l_out), [cnt] "+s"(cnt),
+                           [soffk] "=&s"(soffk), [soffv] "=&s"(soffv)
+                         : [qf] FA_FWD128_C_QF(qall), [kaddr] FA_FWD128_C_KADDR(kaddr),
+                           [vaddr] FA_FWD128_C_VADDR(vaddr), [kw] FA_FWD128_C_KW(kw), [vw] FA_FWD128_C_VW(vw),
+                           [ld0] FA_FWD128_C_LD0(ld0), [ld1] FA_FWD128_C_LD1(ld1), [c] "s"(scale_log2),
+                           [krs] "s"(krw), [vrs] "s"(vrw)
+                         : FA_FWD128_CLOBBERS);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                oacc[0][i] = olo[i];
+                oacc[1][i] = olo[16 + i];
+                oacc[2][i] = ohi[i];
+                oacc[3][i] = ohi[16 + i];
+            }
+            m = m_out;
+            mneg = mneg_out;
+            l = l_out;
+            // Only the thread index stays in a register across the statement
+            // (which leaves the compiler a few VGPRs); everything derived from
+            // it is derived again here.
+            asm volatile("" : "+v"(tid));
+            lane = tid & 63;
+            lq = lane & 31;
+            h = lane >> 5;
+            qrow = qw0 + lq;
+            ld_off = ((tid / DCH) * D + 8 * (tid % DCH)) * 2;
+            k_off = lq * KS + 8 * h;
+            v_off = tr_row(lane) * VS + tr_col(lane);
+        }
+    } else {
+        // (A zero the compiler cannot see through: a constant accumulator
+        // initialisation is otherwise hoisted out of the task loop and held,
+        // or spilled, across it.)
+        float zero = 0.f;
+        asm volatile("" : "+v"(zero));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] = zero;
+        m = -INFINITY;
+        mneg = 0.f;
+        l = 0.f;
+        store_tile(0);
+        __syncthreads();
+    }
     // One key tile.  MASKED tiles may cross a wave's diagonal or the ragged
     // end; the others carry no masking code at all, so no branch splits their
     // loop body and the compiler schedules the scores, the softmax and P V
@@ -233,9 +377,9 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
         store_tile(buf ^ 1);  // buffers last read in the previous tile
         __syncthreads();
     };
-    // Tiles before j_split are wholly visible to every wave of the workgroup.
-    const int j_split = CAUSAL ? min(ntiles, q0 / BC) : (N % BC ? ntiles - 1 : ntiles);
-    for (int j = 0; j < j_split; ++j) step(j, std::false_type{});
+    // (With the assembly loop every unmasked tile has run above.)
+    if constexpr (!kAsmLoop)
+        for (int j = 0; j < j_split; ++j) step(j, std::false_type{});
     for (int j = j_split; j < ntiles; ++j) step(j, std::true_type{});
 
     // Epilogue: O = acc / l, L = (m + log2 l) ln 2.
@@ -254,6 +398,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
             }
         if (h == 0) LSE[(int64_t)bh * N + qrow] = (m + fast_log2(lt)) * kLn2;
     }
+    // Nothing outstanding at the next task's start (the compiler's wait
+    // insertion would otherwise carry this task's stores into the next
+    // task's load waits).
+    wait_vmem_loads();
+    }  // task loop
 }
 
 // fp32 forward: the same loop with every product in fp32 on
@@ -384,12 +533,41 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_f32_kernel(
 
 }  // namespace
 
+int persistent_per_xcd(int tasks, int blocks_per_cu) {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cu_count[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    int cus = (dev >= 0 && dev < kMaxDev) ? cu_count[dev].load(std::memory_order_relaxed) : 0;
+    if (cus <= 0) {
+        if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        if (dev >= 0 && dev < kMaxDev) cu_count[dev].store(cus, std::memory_order_relaxed);
+    }
+    const int per_xcd_tasks = (tasks + kNumXcd - 1) / kNumXcd;
+    return std::max(1, std::min(per_xcd_tasks, std::max(1, blocks_per_cu) * std::max(1, cus / kNumXcd)));
+}
+
+namespace {
+// Workgroups of one kernel that fit on a CU at once (cached per kernel).
+template <typename Kern>
+int blocks_per_cu(Kern kernel, int threads) {
+    static std::atomic<int> cached{0};
+    int n = cached.load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) n = 1;
+        cached.store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+}  // namespace
+
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                            int Hkv, int N, int d, float scale, bool causal, const DropoutParams* dropout,
                            hipStream_t stream) {
     const int BH = B * Hq, G = Hq / Hkv;
     const int nqb = (N + kFwdBr - 1) / kFwdBr;
-    const int grid = grid_for_tasks(nqb * BH);
     const ScoreScale ss = make_score_scale(scale, 1.f, 0x80008000u);
     auto Q = static_cast<const bf16*>(q);
     auto K = static_cast<const bf16*>(k);
@@ -398,8 +576,9 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     const DropoutParams dp = dropout ? *dropout : DropoutParams{0u, 1.f, 0u, 0u, 0u};
 #define FA_FWD_LAUNCH(DD, CC, DR)                                                                          \
     do {                                                                                                   \
-        hipLaunchKernelGGL((fwd_bf16_kernel<DD, CC, DR>), dim3(grid), dim3(kFwdThreads), 0, stream, Q, K, V, \
-                           Op, lse, N, BH, nqb, ss, Hq, G, dp);                                           \
+        const int nx = persistent_per_xcd(nqb * BH, blocks_per_cu(fwd_bf16_kernel<DD, CC, DR>, kFwdThreads)); \
+        hipLaunchKernelGGL((fwd_bf16_kernel<DD, CC, DR>), dim3(kNumXcd * nx), dim3(kFwdThreads), 0, stream, Q, \
+                           K, V, Op, lse, N, BH, nqb, ss, Hq, G, dp, nx);                                 \
         return hipGetLastError();                                                                          \
     } while (0)
 #define FA_FWD_DROP(DD, CC)             \

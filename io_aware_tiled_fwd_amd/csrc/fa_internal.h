@@ -10,6 +10,12 @@
 
 namespace fa {
 
+// Workgroups per XCD for a persistent launch over `tasks` tasks: as many as
+// fit on the XCD's CUs at once (blocks_per_cu per CU of the current device,
+// whose compute units are split evenly over the 8 XCDs), fewer for small
+// grids.  The grid is kNumXcd times this.
+int persistent_per_xcd(int tasks, int blocks_per_cu);
+
 // Forward, bf16 in/out.  d in {64, 128}.  dropout: null for none.
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                            int Hkv, int N, int d, float scale, bool causal, const DropoutParams* dropout,
