@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     OutT* __restrict__ dKout, OutT* __restrict__ dVout, int N, int BKV, int nkb, ScoreScale ss, float dk_scale,
-    float dv_scale, int Hq, int G_arg, DropoutParams drop) {
+    float dv_scale, int Hq, int G_arg, DropoutParams drop, int nx) {
     const float scale_log2 = ss.c;
     static_assert(D == 128, "the paired kernel is built for d = 128");
     const int G = GROUPED ? G_arg : 1;
@@ -437,15 +437,24 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
     __shared__ __attribute__((aligned(16))) f32x4 sP[kPairs][NQH][4][64];
     __shared__ __attribute__((aligned(16))) uint32_t sKeep[DROPOUT ? kPairs : 1][32];
 
-    const int tid = thread_id(), lane = tid & 63, w = wave_id();
-    const int lq = lane & 31, h = lane >> 5;
+    const int w = wave_id();
     // Wavefronts w and w + 4 share a SIMD (measured: pairing w with w + 1
     // instead is 7% slower), so each SIMD runs one wavefront of each role.
     const bool dvw = w < kPairs;  // wave-uniform role
     const int pr = dvw ? w : w - kPairs;
-    // Flat id -> (key/value head, key block) as in the separate kernels.
-    const int task = xcd_task(block_id(), BKV * nkb);
-    if (task >= BKV * nkb) return;
+    // Persistent workgroups (nx per XCD) over the XCD's (key/value head, key
+    // block) tasks in snake order, as in the forward.
+    const int xi = block_id() % kNumXcd, ci = block_id() / kNumXcd;
+    for (int round = 0;; ++round) {
+    const int slot = round * nx + ((round & 1) ? nx - 1 - ci : ci);
+    if (slot >= xcd_tasks(BKV * nkb)) break;  // past this XCD's share
+    const int task = xcd_task(slot * kNumXcd + xi, BKV * nkb);
+    if (task >= BKV * nkb) break;
+    // (Lane offsets recomputed per task: hoisted out of the task loop they
+    // would stay live across it.)
+    int tid = thread_id();
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, lq = lane & 31, h = lane >> 5;
     const int kvh = task / nkb;
     const int kb = task % nkb;
     const int k0 = kb * kFusedBkv;
@@ -734,6 +743,10 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                 store_grad4(op + 32 * db + 8 * r, f32x4{acc[db][4 * r] * os, acc[db][4 * r + 1] * os,
                                                         acc[db][4 * r + 2] * os, acc[db][4 * r + 3] * os});
     }
+    // The dK wavefronts' last products read LDS after the last step's
+    // barrier; the next task stages over it.
+    __syncthreads();
+    }  // task loop
 }
 
 // ---------------------------------------------------------------------------
@@ -756,7 +769,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     OutT* __restrict__ dQ, int N, int BH, int nqb, ScoreScale ss, float scale, int Hq, int G,
-    DropoutParams drop) {
+    DropoutParams drop, int nx) {
     const float scale_log2 = ss.c;
     constexpr int BKV = kDqBkv;
     constexpr int KS = both_ways_stride<D>();
@@ -764,10 +777,18 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
     __shared__ __attribute__((aligned(16))) bf16 sK[2][BKV * KS];
     __shared__ __attribute__((aligned(16))) bf16 sV[2][BKV * VS];
 
-    const int tid = thread_id(), lane = tid & 63, w = wave_id();
-    const int lq = lane & 31, h = lane >> 5;
+    const int w = wave_id();
+    // Persistent workgroups over the XCD's (head, query block) tasks in
+    // snake order, as in the forward.
+    const int xi = block_id() % kNumXcd, ci = block_id() / kNumXcd;
+    for (int round = 0;; ++round) {
+    const int slot = round * nx + ((round & 1) ? nx - 1 - ci : ci);
+    if (slot >= xcd_tasks(BH * nqb)) break;  // past this XCD's share
     int bh, qb;
-    if (!wg_coords(block_id(), BH, nqb, CAUSAL, bh, qb)) return;  // heaviest query blocks first
+    if (!wg_coords(slot * kNumXcd + xi, BH, nqb, CAUSAL, bh, qb)) break;  // heaviest query blocks first
+    int tid = thread_id();
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, lq = lane & 31, h = lane >> 5;
     const int q0 = qb * kDqBq;
     const int qw0 = q0 + 32 * w;
     const int qrow = qw0 + lq;
@@ -897,6 +918,9 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
                             f32x4{dqacc[db][4 * r] * scale, dqacc[db][4 * r + 1] * scale,
                                   dqacc[db][4 * r + 2] * scale, dqacc[db][4 * r + 3] * scale});
     }
+    // (The last step ended on a barrier after its last LDS read, so the next
+    // task may stage at once.)
+    }  // task loop
 }
 
 template <int D>
@@ -932,16 +956,19 @@ hipError_t launch_dkdv_fused_d(const bf16* q, const bf16* k, const bf16* v, cons
                                const float* delta, OutT* dk, OutT* dv, int B, int Hq, int Hkv, int N, float scale,
                                const DropoutParams& dp, hipStream_t stream) {
     const int nkb = (N + kFusedBkv - 1) / kFusedBkv, BKV = B * Hkv;
-    const dim3 grid(grid_for_tasks(nkb * BKV));
     const float dv_scale = DROPOUT ? dp.keep_scale : 1.0f;
-    if (Hq == Hkv)
-        hipLaunchKernelGGL((bwd_dkdv_fused_kernel<D, CAUSAL, false, DROPOUT, OutT>), grid, dim3(kBwdThreads), 0,
-                           stream, q, k, v, dout, lse, delta, dk, dv, N, BKV, nkb, make_score_scale(scale, 1.f, 0x80008000u), scale, dv_scale,
-                           Hq, 1, dp);
-    else
-        hipLaunchKernelGGL((bwd_dkdv_fused_kernel<D, CAUSAL, true, DROPOUT, OutT>), grid, dim3(kBwdThreads), 0,
-                           stream, q, k, v, dout, lse, delta, dk, dv, N, BKV, nkb, make_score_scale(scale, 1.f, 0x80008000u), scale, dv_scale,
-                           Hq, Hq / Hkv, dp);
+    const ScoreScale ss = make_score_scale(scale, 1.f, 0x80008000u);
+    if (Hq == Hkv) {
+        auto kern = bwd_dkdv_fused_kernel<D, CAUSAL, false, DROPOUT, OutT>;
+        const int nx = persistent_per_xcd(nkb * BKV, blocks_per_cu(kern, kBwdThreads));
+        hipLaunchKernelGGL(kern, dim3(kNumXcd * nx), dim3(kBwdThreads), 0, stream, q, k, v, dout, lse, delta, dk, dv,
+                           N, BKV, nkb, ss, scale, dv_scale, Hq, 1, dp, nx);
+    } else {
+        auto kern = bwd_dkdv_fused_kernel<D, CAUSAL, true, DROPOUT, OutT>;
+        const int nx = persistent_per_xcd(nkb * BKV, blocks_per_cu(kern, kBwdThreads));
+        hipLaunchKernelGGL(kern, dim3(kNumXcd * nx), dim3(kBwdThreads), 0, stream, q, k, v, dout, lse, delta, dk, dv,
+                           N, BKV, nkb, ss, scale, dv_scale, Hq, Hq / Hkv, dp, nx);
+    }
     return hipGetLastError();
 }
 template <int D, bool CAUSAL>
@@ -977,20 +1004,16 @@ hipError_t launch_dq_t(const bf16* q, const bf16* k, const bf16* v, const float*
                        const float* delta, void* dq, int B, int Hq, int Hkv, int N, float scale,
                        const DropoutParams* dropout, bool grad_bf16, hipStream_t stream) {
     const int nqb = (N + kDqBq - 1) / kDqBq, BH = B * Hq;
-    const dim3 grid(grid_for_tasks(nqb * BH));
-    if (grad_bf16)
-        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, bf16>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                           lse, delta, static_cast<bf16*>(dq), N, BH, nqb, make_score_scale(scale, 1.f, 0x80008000u), scale, Hq, Hq / Hkv,
-                           kNoDropout);
-    else if (dropout)
-        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true, float>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                           lse, delta, static_cast<float*>(dq), N, BH, nqb, make_score_scale(scale, 1.f, 0x80008000u), scale, Hq, Hq / Hkv,
-                           *dropout);
-    else
-        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, float>), grid, dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                           lse, delta, static_cast<float*>(dq), N, BH, nqb, make_score_scale(scale, 1.f, 0x80008000u), scale, Hq, Hq / Hkv,
-                           kNoDropout);
-    return hipGetLastError();
+    const ScoreScale ss = make_score_scale(scale, 1.f, 0x80008000u);
+    auto launch = [&](auto kern, auto* out, const DropoutParams& dp) {
+        const int nx = persistent_per_xcd(nqb * BH, blocks_per_cu(kern, kBwdThreads));
+        hipLaunchKernelGGL(kern, dim3(kNumXcd * nx), dim3(kBwdThreads), 0, stream, q, k, v, dout, lse, delta, out, N,
+                           BH, nqb, ss, scale, Hq, Hq / Hkv, dp, nx);
+        return hipGetLastError();
+    };
+    if (grad_bf16) return launch(bwd_dq_kernel<D, CAUSAL, false, bf16>, static_cast<bf16*>(dq), kNoDropout);
+    if (dropout) return launch(bwd_dq_kernel<D, CAUSAL, true, float>, static_cast<float*>(dq), *dropout);
+    return launch(bwd_dq_kernel<D, CAUSAL, false, float>, static_cast<float*>(dq), kNoDropout);
 }
 
 }  // namespace

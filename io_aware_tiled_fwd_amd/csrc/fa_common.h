@@ -96,6 +96,10 @@ __device__ __forceinline__ int xcd_task(int id, int total) {
     const int per = (total + kNumXcd - 1) / kNumXcd;
     return (id % kNumXcd) * per + id / kNumXcd;
 }
+// Tasks per XCD under xcd_task and head_rank: an XCD's k-th workgroup has a
+// task of its own only for k below this (beyond it xcd_task continues into
+// the next XCD's range, which that XCD's workgroups cover).
+__device__ __forceinline__ int xcd_tasks(int total) { return (total + kNumXcd - 1) / kNumXcd; }
 
 // Map a flat workgroup id to (head, rank) for a grid of grid_for_tasks(nheads
 // * nranks) workgroups, rank 0 being a head's heaviest block.  When nheads is

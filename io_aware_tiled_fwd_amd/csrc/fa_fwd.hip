@@ -110,6 +110,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     const int xi = block_id() % kNumXcd, ci = block_id() / kNumXcd;
     for (int round = 0;; ++round) {
     const int task = round * nx + ((round & 1) ? nx - 1 - ci : ci);
+    if (task >= xcd_tasks(BH * nqb)) break;  // past this XCD's share
     int bh, qb;
     if (!wg_coords(task * kNumXcd + xi, BH, nqb, CAUSAL, bh, qb)) break;
     // The lane's offsets are recomputed for every task (the empty asm hides
@@ -549,19 +550,6 @@ int persistent_per_xcd(int tasks, int blocks_per_cu) {
     return std::max(1, std::min(per_xcd_tasks, std::max(1, blocks_per_cu) * std::max(1, cus / kNumXcd)));
 }
 
-namespace {
-// Workgroups of one kernel that fit on a CU at once (cached per kernel).
-template <typename Kern>
-int blocks_per_cu(Kern kernel, int threads) {
-    static std::atomic<int> cached{0};
-    int n = cached.load(std::memory_order_relaxed);
-    if (n <= 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) n = 1;
-        cached.store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-}  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                            int Hkv, int N, int d, float scale, bool causal, const DropoutParams* dropout,

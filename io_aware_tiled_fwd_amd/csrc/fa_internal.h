@@ -6,6 +6,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "fa_common.h"
 
 namespace fa {
@@ -15,6 +17,18 @@ namespace fa {
 // whose compute units are split evenly over the 8 XCDs), fewer for small
 // grids.  The grid is kNumXcd times this.
 int persistent_per_xcd(int tasks, int blocks_per_cu);
+
+// Workgroups of one kernel that fit on a CU at once (cached per kernel).
+template <typename Kern>
+int blocks_per_cu(Kern kernel, int threads) {
+    static std::atomic<int> cached{0};
+    int n = cached.load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) n = 1;
+        cached.store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 // Forward, bf16 in/out.  d in {64, 128}.  dropout: null for none.
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
