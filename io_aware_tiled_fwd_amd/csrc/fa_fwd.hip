@@ -37,6 +37,7 @@
 // taking its XCD's (head, query block) tasks in snake order.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "fa_common.h"
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     __shared__ __attribute__((aligned(16))) bf16 sV[2][BC * VS];
 
     const int w = wave_id();
-    // Persistent workgroups: nx per XCD, at most one per CU.  Workgroup ci of
+    // Persistent workgroups: nx per XCD, as many as fit at once.  Workgroup ci of
     // XCD xi takes the XCD's tasks (wg_coords order: a head's query blocks
     // together, heaviest first) in snake order -- ci, then 2 nx - 1 - ci, then
     // 2 nx + ci, ... -- so that a heavy task and a light one alternate on every
@@ -533,6 +534,25 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_f32_kernel(
 }
 
 }  // namespace
+
+int blocks_per_cu_of(const void* kernel, int threads) {
+    constexpr int kSlots = 256;
+    static std::mutex mu;
+    static const void* keys[kSlots];
+    static int vals[kSlots];
+    static int used = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+        if (keys[i] == kernel) return vals[i];
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) n = 1;
+    if (used < kSlots) {
+        keys[used] = kernel;
+        vals[used] = n;
+        ++used;
+    }
+    return n;
+}
 
 int persistent_per_xcd(int tasks, int blocks_per_cu) {
     constexpr int kMaxDev = 64;

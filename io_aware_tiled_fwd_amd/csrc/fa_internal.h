@@ -6,8 +6,6 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
-#include <atomic>
-
 #include "fa_common.h"
 
 namespace fa {
@@ -18,16 +16,13 @@ namespace fa {
 // grids.  The grid is kNumXcd times this.
 int persistent_per_xcd(int tasks, int blocks_per_cu);
 
-// Workgroups of one kernel that fit on a CU at once (cached per kernel).
+// Workgroups of one kernel that fit on a CU at once, looked up once per
+// kernel (keyed by its address: instantiations that share a signature differ
+// in their register and LDS use).
+int blocks_per_cu_of(const void* kernel, int threads);
 template <typename Kern>
 int blocks_per_cu(Kern kernel, int threads) {
-    static std::atomic<int> cached{0};
-    int n = cached.load(std::memory_order_relaxed);
-    if (n <= 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) n = 1;
-        cached.store(n, std::memory_order_relaxed);
-    }
-    return n;
+    return blocks_per_cu_of(reinterpret_cast<const void*>(kernel), threads);
 }
 
 // Forward, bf16 in/out.  d in {64, 128}.  dropout: null for none.

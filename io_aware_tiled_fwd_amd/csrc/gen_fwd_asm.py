@@ -37,35 +37,50 @@ pairs on gfx950.
 import os
 import sys
 
-D = 128
-BC = 64
-KS = D + 8            # K row stride in LDS (elements)
-VS = D + 32           # V row stride in LDS (elements)
-KBUF = BC * KS * 2    # bytes of one K buffer
-VBUF = BC * VS * 2    # bytes of one V buffer
-K_KB = 32 * KS * 2    # the second 32-key half of a K tile
-V_S2 = 16 * VS * 2    # a 16-key k-step of V
-V_HALF = 8 * VS * 2   # the second transposing read of a fragment
-K_CH = 32 * KS * 2    # the second staging chunk (32 rows on)
-V_CH = 32 * VS * 2
-TILE_BYTES = BC * D * 2
+BC = 64               # keys per tile
 
-# VGPR map (see fa_fwd.hip for the operands bound to them).
-O = 0                 # v[0:63]    O^T accumulators, block db in v[16 db : 16 db + 15]
-S = (64, 96)          # v[64:127]  two score buffers, half kb in v[S + 16 kb : +15]
-QF = 128              # v[128:159] Q^T operand, k-step ks in v[QF + 4 ks : +3]
-NKR = 5               # K fragment ring (slots of 4)
-NVR = 5               # V^T fragment ring
-KR = 160
-VR = KR + 4 * NKR
-KST = VR + 4 * NVR    # staged K rows (2 chunks of 4)
-VST = KST + 8         # staged V rows
-M, MNEG, L, RS0, RS1, T0, T1, T2 = range(VST + 8, VST + 16)
-KADDR, VADDR, KW, VW, LD0, LD1 = range(VST + 16, VST + 22)
-K1ST = 96             # K(1) staged in the prologue (score buffer 1 is free then)
-NVGPR = LD1 + 1
 
-# Wait states required between the two instructions (s_nop N gives N + 1).
+def configure(d):
+    """Sets the module's layout and register map for head dimension d (64 or
+    128); every function below reads them."""
+    g = globals()
+    g["D"] = d
+    g["NKS"] = d // 16               # k-steps of the score chains
+    g["NDB"] = d // 32               # 32-dimension blocks of O
+    g["CH"] = BC * d // 8 // 512     # staged 16-byte chunks per thread and tensor
+    g["KS"] = d + 8                  # K row stride in LDS (elements)
+    g["VS"] = d + 32                 # V row stride in LDS (elements)
+    g["KBUF"] = BC * g["KS"] * 2     # bytes of one K buffer
+    g["VBUF"] = BC * g["VS"] * 2     # bytes of one V buffer
+    g["K_KB"] = 32 * g["KS"] * 2     # the second 32-key half of a K tile
+    g["V_S2"] = 16 * g["VS"] * 2     # a 16-key k-step of V
+    g["V_HALF"] = 8 * g["VS"] * 2    # the second transposing read of a fragment
+    g["K_CH"] = 32 * g["KS"] * 2     # the second staging chunk (32 rows on)
+    g["V_CH"] = 32 * g["VS"] * 2
+    g["TILE_BYTES"] = BC * d * 2
+    # VGPR map (fa_fwd.hip binds the operands to these registers):
+    #   O    O^T accumulators, block db in v[O + 16 db : +15]
+    #   S    two score buffers of 32, key half kb in v[S + 16 kb : +15]
+    #   QF   Q^T operand, k-step ks in v[QF + 4 ks : +3]
+    #   KR, VR   K and V^T fragment rings (slots of 4)
+    #   KST, VST staged K and V rows (CH chunks of 4)
+    g["O"] = 0
+    g["S"] = (d // 2, d // 2 + 32)
+    g["QF"] = d // 2 + 64
+    g["KR"] = g["QF"] + 4 * g["NKS"]
+    g["VR"] = g["KR"] + 4 * NKR
+    g["KST"] = g["VR"] + 4 * NVR
+    g["VST"] = g["KST"] + 4 * g["CH"]
+    base = g["VST"] + 4 * g["CH"]
+    (g["M"], g["MNEG"], g["L"], g["RS0"], g["RS1"], g["T0"], g["T1"], g["T2"]) = range(base, base + 8)
+    (g["KADDR"], g["VADDR"], g["KW"], g["VW"], g["LD0"], g["LD1"]) = range(base + 8, base + 14)
+    g["K1ST"] = g["S"][1]            # K(1) staged in the prologue (score buffer 1 is free then)
+    g["NVGPR"] = g["LD1"] + 1
+
+
+NKR = 5               # K fragment ring slots
+NVR = 5               # V^T fragment ring slots
+
 MFMA_VALU_WS = 12     # MFMA result -> other instruction
 VALU_MFMA_WS = 2      # VALU result -> MFMA operand
 VALU_PERM_WS = 2      # VALU result -> v_permlane32_swap
@@ -214,7 +229,7 @@ def rescale_block():
     out.append(valu(f"v_mov_b32 {vr(M)}, {vr(T1)}", [T1], [M]))
     out.append(valu(f"v_xor_b32 {vr(MNEG)}, 0x80000000, {vr(T1)}", [T1], [MNEG]))
     out.append(valu(f"v_mul_f32 {vr(L)}, {vr(L)}, {vr(T2)}", [L, T2], [L]))
-    for x in range(O, O + 64):
+    for x in range(O, O + 16 * NDB):
         out.append(valu(f"v_mul_f32 {vr(x)}, {vr(T2)}, {vr(x)}", [T2, x], [x]))
     return out
 
@@ -239,7 +254,7 @@ def mfma_stream(p, pattern, with_scores, kbuf, vbuf):
     reads issued right after it]."""
     sb, sn = S[p], S[p ^ 1]
     s_list = [(kb, ks) for ks in range(D // 16) for kb in range(2)] if with_scores else []
-    pv = [(s2, db) for s2 in range(4) for db in range(4)]
+    pv = [(s2, db) for s2 in range(4) for db in range(NDB)]
     # operand reads, in the order their MFMAs come
     k_reads = []  # (reg, [Ins]) per score MFMA
     for f, (kb, ks) in enumerate(s_list):
@@ -286,6 +301,38 @@ def mfma_stream(p, pattern, with_scores, kbuf, vbuf):
     return pre, slots
 
 
+# Per head dimension: the MFMA order of a steady-state tile ('S': the next
+# score k-step of S(t+1), 'P': the next P V k-step and dimension block), the
+# MFMA slots over which the four softmax parts and the row maximum are spread
+# (first, last slot), and the slots after which the staged rows are stored.
+# At d = 128 a tile has 32 MFMAs and ~4 VALU instructions per MFMA.  (A d = 64
+# schedule -- 16 MFMAs for the same softmax, so the VALU work sets the pace --
+# ran no faster than the compiler's schedule of the same step and is not
+# emitted.)
+SCHEDULE = {
+    128: dict(pattern="S" * 7 + "P" * 4 + "S" * 3 + "P" * 4 + "S" * 6 + "P" * 8,
+              parts=((0, 5), (6, 12), (13, 19), (20, 26)), rowmax=(27, 31), stores=(8, 14, 20, 26)),
+}
+
+
+def staged_stores(p):
+    """The stores of one tile's staged rows (K(t+2) into K buffer p, V(t+1)
+    into V buffer p^1), each followed by the load of the same rows one tile
+    on, chunk by chunk: [K chunks..., V chunks...]."""
+    groups = []
+    for r in range(CH):
+        g = [ds_write(KW, KST + 4 * r, p * KBUF + r * K_CH), buf_load(KST + 4 * r, LD0 + r, "krs", "soffk")]
+        if r == CH - 1:
+            g.append(salu(f"s_add_u32 %[soffk], %[soffk], {TILE_BYTES:#x}"))
+        groups.append(g)
+    for r in range(CH):
+        g = [ds_write(VW, VST + 4 * r, (p ^ 1) * VBUF + r * V_CH), buf_load(VST + 4 * r, LD0 + r, "vrs", "soffv")]
+        if r == CH - 1:
+            g.append(salu(f"s_add_u32 %[soffv], %[soffv], {TILE_BYTES:#x}"))
+        groups.append(g)
+    return groups
+
+
 def tile_iteration(p):
     """Steady-state tile t with S(t) in score buffer p: S(t+1), the softmax
     of S(t), O += V(t)^T P(t)^T, the maximum of S(t+1), the LDS stores of
@@ -293,28 +340,24 @@ def tile_iteration(p):
     K(t+3) and V(t+2), and the barrier.  K(t+1) is in K buffer p^1, V(t) in
     V buffer p; K(t+2) goes to K buffer p, V(t+1) to V buffer p^1."""
     sb, sn = S[p], S[p ^ 1]
+    sch = SCHEDULE[D]
     out = []
-    pattern = "S" * 7 + "P" * 4 + "S" * 3 + "P" * 4 + "S" * 6 + "P" * 8
-    pre, slots = mfma_stream(p, pattern, True, p ^ 1, p)
+    pre, slots = mfma_stream(p, sch["pattern"], True, p ^ 1, p)
     parts = [softmax_part(sb, s2) for s2 in range(4)]
     out += pre
     # the first part starts before the first MFMA (its K operand is in flight)
     out += parts[0][:8]
-    spread(parts[0][8:], slots, 0, 5)
-    spread(parts[1], slots, 6, 12)
-    spread(parts[2], slots, 13, 19)
-    spread(parts[3] + row_sum_close(), slots, 20, 26)
-    spread(row_max(sn), slots, 27, 31)
-    # LDS stores of the staged rows, spread over the tile (after MFMA slots 8,
-    # 14, 20, 26): K(t+2) overwrites K(t), read in the previous tile; V(t+1)
-    # overwrites V(t-1).  Each store frees its registers for the global load
-    # of the same rows one tile on, which then has a whole tile to arrive.
-    slots[8] += [ds_write(KW, KST, p * KBUF), buf_load(KST, LD0, "krs", "soffk")]
-    slots[14] += [ds_write(KW, KST + 4, p * KBUF + K_CH), buf_load(KST + 4, LD1, "krs", "soffk"),
-                  salu("s_add_u32 %[soffk], %[soffk], 0x4000")]
-    slots[20] += [ds_write(VW, VST, (p ^ 1) * VBUF), buf_load(VST, LD0, "vrs", "soffv")]
-    slots[26] += [ds_write(VW, VST + 4, (p ^ 1) * VBUF + V_CH), buf_load(VST + 4, LD1, "vrs", "soffv"),
-                  salu("s_add_u32 %[soffv], %[soffv], 0x4000")]
+    parts[0] = parts[0][8:]
+    parts[3] = parts[3] + row_sum_close()
+    for part, (first, last) in zip(parts, sch["parts"]):
+        spread(part, slots, first, last)
+    spread(row_max(sn), slots, *sch["rowmax"])
+    # LDS stores of the staged rows, spread over the tile: K(t+2) overwrites
+    # K(t), read in the previous tile; V(t+1) overwrites V(t-1).  Each store
+    # frees its registers for the global load of the same rows one tile on,
+    # which then has a whole tile to arrive.
+    for g, slot in zip(staged_stores(p), sch["stores"]):
+        slots[slot] += g
     for s in slots:
         out += s
     out += row_max_close() + rescale_test()
@@ -328,15 +371,15 @@ def tile_last(p):
     for the masked tiles that follow, and ends on a barrier."""
     sb = S[p]
     out = []
-    pre, slots = mfma_stream(p, "P" * 16, False, None, p)
+    pre, slots = mfma_stream(p, "P" * (4 * NDB), False, None, p)
     parts = [softmax_part(sb, s2) for s2 in range(4)]
     out += pre + parts[0]
-    spread(parts[1], slots, 0, 3)
-    spread(parts[2], slots, 4, 7)
-    spread(parts[3] + row_sum_close(), slots, 8, 11)
+    for s2 in range(1, 4):  # part s2 beside the P V MFMAs of k-step s2 - 1
+        extra = row_sum_close() if s2 == 3 else []
+        spread(parts[s2] + extra, slots, NDB * (s2 - 1), NDB * s2 - 1)
     for s in slots:
         out += s
-    out += [ds_write(VW, VST, (p ^ 1) * VBUF), ds_write(VW, VST + 4, (p ^ 1) * VBUF + V_CH)]
+    out += [ds_write(VW, VST + 4 * r, (p ^ 1) * VBUF + r * V_CH) for r in range(CH)]
     # (K(t+2) was loaded too, for nothing: the masked tiles stage their own.)
     out += [raw("s_waitcnt vmcnt(0) lgkmcnt(0)", "wait"), raw("s_barrier", "barrier")]
     return out
@@ -345,16 +388,16 @@ def tile_last(p):
 def prologue():
     """K(0), V(0) and K(1), already loaded into registers, go to LDS; then
     S(0) into score buffer 0, its maximum as the first reference m, O = 0."""
-    out = [ds_write(KW, KST, 0), ds_write(KW, KST + 4, K_CH),
-           ds_write(VW, VST, 0), ds_write(VW, VST + 4, V_CH),
-           ds_write(KW, K1ST, KBUF), ds_write(KW, K1ST + 4, KBUF + K_CH),
-           salu("s_mov_b32 %[soffk], 0x8000"), salu("s_mov_b32 %[soffv], 0x4000"),
-           buf_load(KST, LD0, "krs", "soffk"), buf_load(KST + 4, LD1, "krs", "soffk"),
-           buf_load(VST, LD0, "vrs", "soffv"), buf_load(VST + 4, LD1, "vrs", "soffv"),
-           raw("s_waitcnt lgkmcnt(0)", "wait"), raw("s_barrier", "barrier")]
+    out = [ds_write(KW, KST + 4 * r, r * K_CH) for r in range(CH)]
+    out += [ds_write(VW, VST + 4 * r, r * V_CH) for r in range(CH)]
+    out += [ds_write(KW, K1ST + 4 * r, KBUF + r * K_CH) for r in range(CH)]
+    out += [salu(f"s_mov_b32 %[soffk], {2 * TILE_BYTES:#x}"), salu(f"s_mov_b32 %[soffv], {TILE_BYTES:#x}")]
+    out += [buf_load(KST + 4 * r, LD0 + r, "krs", "soffk") for r in range(CH)]
+    out += [buf_load(VST + 4 * r, LD0 + r, "vrs", "soffv") for r in range(CH)]
+    out += [raw("s_waitcnt lgkmcnt(0)", "wait"), raw("s_barrier", "barrier")]
     # S(0): the score chains alone (buffer 1 of the scores is idle: use the
     # generic stream with a P V-free pattern)
-    s_list = [(kb, ks) for ks in range(D // 16) for kb in range(2)]
+    s_list = [(kb, ks) for ks in range(NKS) for kb in range(2)]
     reads = []
     for f, (kb, ks) in enumerate(s_list):
         reg = KR + 4 * (f % NKR)
@@ -368,15 +411,15 @@ def prologue():
         if f + NKR < len(reads):
             s.append(reads[f + NKR][1])
         slots.append(s)
-    zero = [valu(f"v_mov_b32 {vr(x)}, 0", [], [x]) for x in range(O, O + 64)]
+    zero = [valu(f"v_mov_b32 {vr(x)}, 0", [], [x]) for x in range(O, O + 16 * NDB)]
     zero += [valu(f"v_mov_b32 {vr(L)}, 0", [], [L])]
-    spread(zero, slots, 0, 15)
+    spread(zero, slots, 0, len(slots) - 1)
     for s in slots:
         out += s
     out += row_max(S[0]) + row_max_close()
     out += [valu(f"v_mov_b32 {vr(M)}, {vr(T1)}", [T1], [M]),
             valu(f"v_xor_b32 {vr(MNEG)}, 0x80000000, {vr(T1)}", [T1], [MNEG]),
-            salu("s_mov_b32 %[soffk], 0xc000"), salu("s_mov_b32 %[soffv], 0x8000")]
+            salu(f"s_mov_b32 %[soffk], {3 * TILE_BYTES:#x}"), salu(f"s_mov_b32 %[soffv], {2 * TILE_BYTES:#x}")]
     # The first tile stores K(2) over K(0): every wavefront must have read
     # K(0) by then.
     out += [raw("s_barrier", "barrier")]
@@ -561,7 +604,10 @@ def _branch_target(text):
     return parts[1] if parts[0].startswith("s_cbranch") or parts[0] == "s_branch" else None
 
 
-ALL_FRESH = ({r: (0, "mfma") for r in range(NVGPR)}, {r: 0 for r in range(NVGPR)}, None)
+def _all_fresh():
+    """The state at a label no branch has reached yet: every register just
+    written by an MFMA and read as an accumulator."""
+    return ({r: (0, "mfma") for r in range(NVGPR)}, {r: 0 for r in range(NVGPR)}, None)
 
 
 def assemble():
@@ -579,7 +625,7 @@ def assemble():
         for ins in prog:
             if ins.kind == "label":
                 name = ins.text.rstrip(":")
-                snaps = list(at_branch.get(name, [ALL_FRESH]))
+                snaps = list(at_branch.get(name, [_all_fresh()]))
                 if prev_fall:
                     snaps.append(_snapshot(f))
                 assert not f.lds, f"LDS operations outstanding at {name}"
@@ -603,33 +649,45 @@ def assemble():
 
 
 def clobbers():
-    pinned = set(range(O, O + 64)) | set(range(QF, QF + 32)) | set(range(KST, KST + 16)) | set(range(K1ST, K1ST + 8))
+    pinned = set(range(O, O + 16 * NDB)) | set(range(QF, QF + 4 * NKS)) | set(range(KST, KST + 8 * CH))
+    pinned |= set(range(K1ST, K1ST + 4 * CH))
     pinned |= {M, MNEG, L, KADDR, VADDR, KW, VW, LD0, LD1}
     return [f"v{r}" for r in range(NVGPR) if r not in pinned]
+
+
+def emit(fh, d):
+    configure(d)
+    lines = assemble()
+    pre = f"FA_FWD{d}"
+    fh.write(f"// d = {d}: VGPRs v0..v{NVGPR - 1}.\n")
+    fh.write(f"#define {pre}_NVGPR {NVGPR}\n")
+    # register constraints of the operands bound to the asm statement
+    cons = {"QF": vr(QF, 4 * NKS), "KST": vr(KST, 4 * CH), "VST": vr(VST, 4 * CH), "K1ST": vr(K1ST, 4 * CH),
+            "M": vr(M), "MNEG": vr(MNEG), "L": vr(L), "KADDR": vr(KADDR), "VADDR": vr(VADDR), "KW": vr(KW),
+            "VW": vr(VW), "LD0": vr(LD0), "LD1": vr(LD1)}
+    if NDB == 4:
+        cons.update(OLO=vr(O, 32), OHI=vr(O + 32, 32))
+    else:
+        cons.update(O=vr(O, 16 * NDB))
+    for k, v in cons.items():
+        fh.write(f'#define {pre}_C_{k} "{{{v}}}"\n')
+    fh.write(f"#define {pre}_ASM \\\n")
+    for ln in lines:
+        fh.write(f'    "{ln}\\n" \\\n')
+    fh.write('    ""\n')
+    fh.write(f"#define {pre}_CLOBBERS " + ", ".join(f'"{c}"' for c in clobbers()) + ', "vcc", "scc", "memory"\n')
+    return len(lines)
 
 
 def main():
     dst = sys.argv[1] if len(sys.argv) > 1 else os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                               "fa_fwd_asm.inc")
-    lines = assemble()
     with open(dst, "w") as fh:
         fh.write("// Generated by gen_fwd_asm.py -- do not edit.\n")
-        fh.write("// The hand-scheduled key loop of the bf16 forward at d = 128 (fa_fwd.hip).\n")
-        fh.write(f"// VGPRs v0..v{NVGPR - 1}; register map and schedule in gen_fwd_asm.py.\n")
-        fh.write(f"#define FA_FWD128_NVGPR {NVGPR}\n")
-        # register constraints of the operands bound to the asm statement
-        cons = {"OLO": vr(O, 32), "OHI": vr(O + 32, 32), "QF": vr(QF, 32), "KST": vr(KST, 8), "VST": vr(VST, 8),
-                "K1ST": vr(K1ST, 8), "M": vr(M), "MNEG": vr(MNEG), "L": vr(L), "KADDR": vr(KADDR),
-                "VADDR": vr(VADDR), "KW": vr(KW), "VW": vr(VW), "LD0": vr(LD0), "LD1": vr(LD1)}
-        for k, v in cons.items():
-            fh.write(f'#define FA_FWD128_C_{k} "{{{v}}}"\n')
-        fh.write("#define FA_FWD128_ASM \\\n")
-        for ln in lines:
-            fh.write(f'    "{ln}\\n" \\\n')
-        fh.write('    ""\n')
-        fh.write("#define FA_FWD128_CLOBBERS " + ", ".join(f'"{c}"' for c in clobbers()) +
-                 ', "vcc", "scc", "memory"\n')
-    print(f"wrote {dst}: {len(lines)} lines")
+        fh.write("// The hand-scheduled key loop of the bf16 forward (fa_fwd.hip) for the head\n")
+        fh.write("// dimensions in SCHEDULE; register map and schedule in gen_fwd_asm.py.\n")
+        n = [emit(fh, d) for d in sorted(SCHEDULE, reverse=True)]
+    print(f"wrote {dst}: {n} lines")
 
 
 if __name__ == "__main__":
