@@ -109,11 +109,47 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     // tasks: workgroups are dealt to the XCDs in id order, so an XCD whose CUs
     // are all busy holds back the dispatch of the workgroups behind it.
     const int xi = block_id() % kNumXcd, ci = block_id() / kNumXcd;
-    for (int round = 0;; ++round) {
-    const int task = round * nx + ((round & 1) ? nx - 1 - ci : ci);
-    if (task >= xcd_tasks(BH * nqb)) break;  // past this XCD's share
+    // (head, query block) of this workgroup's task in round r; false past the
+    // XCD's share.
+    auto task_of = [&](int r, int& bh_, int& qb_) -> bool {
+        const int t = r * nx + ((r & 1) ? nx - 1 - ci : ci);
+        if (t >= xcd_tasks(BH * nqb)) return false;
+        return wg_coords(t * kNumXcd + xi, BH, nqb, CAUSAL, bh_, qb_);
+    };
+    constexpr int ROWS_PER_PASS = kFwdThreads / DCH;
+    // The loads that open a task: this wave's Q fragments (the Q^T operand,
+    // k-step ks = Q[row][16 ks + 8 h .. +7]) and the thread's chunks of K(0),
+    // V(0) and K(1).  A task issues them for the next task right behind its
+    // own output stores, so that their latency overlaps the stores' instead of
+    // following it.
+    bf16x8 qf[NKS];
+    u32x4 k0p[CH], v0p[CH], k1p[CH];
+    auto issue_task_loads = [&](int bh_, int qb_) __attribute__((always_inline)) {
+        int t = thread_id();
+        asm volatile("" : "+v"(t));
+        const int ln = t & 63;
+        const uint32_t hb = (uint32_t)N * D * 2;
+        const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + (int64_t)bh_ * N * D, hb);
+        const int64_t kvb = (int64_t)kv_head(bh_, Hq, G) * N * D;
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + kvb, hb);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + kvb, hb);
+        const int qw = qb_ * kFwdBr + 32 * w;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            qf[ks] = __builtin_bit_cast(
+                bf16x8, buffer_load16(qr, ((ln & 31) * D + 16 * ks + 8 * (ln >> 5)) * 2, qw * D * 2));
+        const int lo = ((t / DCH) * D + 8 * (t % DCH)) * 2;
+#pragma unroll
+        for (int r = 0; r < CH; ++r) {
+            k0p[r] = buffer_load16(kr, lo + r * ROWS_PER_PASS * D * 2, 0);
+            v0p[r] = buffer_load16(vr, lo + r * ROWS_PER_PASS * D * 2, 0);
+            k1p[r] = buffer_load16(kr, lo + r * ROWS_PER_PASS * D * 2, BC * D * 2);
+        }
+    };
     int bh, qb;
-    if (!wg_coords(task * kNumXcd + xi, BH, nqb, CAUSAL, bh, qb)) break;
+    if (!task_of(0, bh, qb)) return;
+    issue_task_loads(bh, qb);
+    for (int round = 0;; ++round) {
     // The lane's offsets are recomputed for every task (the empty asm hides
     // that they do not change): hoisted out of the task loop they would stay
     // live across it and push the kernel past its register budget.
@@ -128,17 +164,8 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
 
     // Per-head buffer resources: rows past N read as zero.
     const uint32_t head_bytes = (uint32_t)N * D * 2;
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q + base, head_bytes);
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + kv_base, head_bytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + kv_base, head_bytes);
-
-    // Q^T operand: k-step ks holds Q[qrow][16 ks + 8 h .. +7], carrying the
-    // sign of the scale (ScoreScale) once loaded (below, after the first
-    // tile's loads are issued too).
-    bf16x8 qf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-        qf[ks] = __builtin_bit_cast(bf16x8, buffer_load16(qrs, (lq * D + 16 * ks + 8 * h) * 2, qw0 * D * 2));
 
     // Accumulators and the running statistics: set by the assembly loop, or
     // to their initial values (O = 0, m = -inf, l = 0) before the first
@@ -154,7 +181,6 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     // Staging of tile j+1 through registers, K and V alike as row-major
     // copies: thread chunk r covers row (tid + 512 r) / DCH, 16-byte column
     // tid % DCH.  Tile offsets ride in the scalar offset.
-    constexpr int ROWS_PER_PASS = kFwdThreads / DCH;
     int ld_off = ((tid / DCH) * D + 8 * (tid % DCH)) * 2;
     u32x4 kreg[CH], vreg[CH];
     auto load_tile = [&](int j) {
@@ -196,23 +222,19 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
     // then drains the load counter at the store, so the compiler never makes
     // the math wait on a pending load.
     u32x8 kst, vst, k1st;  // the assembly loop's first tiles: K(0), V(0), K(1)
+    // The task's opening loads (issued by the previous task, or before the
+    // loop) and the previous task's output stores complete here.
+    wait_vmem_loads();
     if (use_asm) {
 #pragma unroll
-        for (int r = 0; r < CH; ++r) {
-            const u32x4 k0r = buffer_load16(krs, ld_off + r * ROWS_PER_PASS * D * 2, 0);
-            const u32x4 v0r = buffer_load16(vrs, ld_off + r * ROWS_PER_PASS * D * 2, 0);
-            const u32x4 k1r = buffer_load16(krs, ld_off + r * ROWS_PER_PASS * D * 2, BC * D * 2);
+        for (int r = 0; r < CH; ++r)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                kst[4 * r + e] = k0r[e];
-                vst[4 * r + e] = v0r[e];
-                k1st[4 * r + e] = k1r[e];
+                kst[4 * r + e] = k0p[r][e];
+                vst[4 * r + e] = v0p[r][e];
+                k1st[4 * r + e] = k1p[r][e];
             }
-        }
-    } else {
-        load_tile(0);
     }
-    wait_vmem_loads();
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = apply_sign(qf[ks], ss);
     if (use_asm) {
@@ -279,6 +301,11 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
         m = -INFINITY;
         mneg = 0.f;
         l = 0.f;
+#pragma unroll
+        for (int r = 0; r < CH; ++r) {
+            kreg[r] = k0p[r];
+            vreg[r] = v0p[r];
+        }
         store_tile(0);
         __syncthreads();
     }
@@ -400,10 +427,15 @@ __global__ __launch_bounds__(kFwdThreads, 1) void fwd_bf16_kernel(
             }
         if (h == 0) LSE[(int64_t)bh * N + qrow] = (m + fast_log2(lt)) * kLn2;
     }
-    // Nothing outstanding at the next task's start (the compiler's wait
-    // insertion would otherwise carry this task's stores into the next
-    // task's load waits).
-    wait_vmem_loads();
+    // The next task's opening loads go out right behind this task's stores,
+    // without waiting for the stores to complete: the wait at the next task's
+    // start then covers both at once.
+    int nbh, nqb_;
+    const bool more = task_of(round + 1, nbh, nqb_);
+    if (!more) break;
+    issue_task_loads(nbh, nqb_);
+    bh = nbh;
+    qb = nqb_;
     }  // task loop
 }
 
