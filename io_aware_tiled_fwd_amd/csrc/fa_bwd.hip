@@ -51,6 +51,18 @@ constexpr int kBwdThreads = 64 * kBwdWaves;
 template <int D>
 constexpr int both_ways_stride() { return D == 128 ? D + 24 : D + 8; }
 
+// The paired dK/dV kernel's tiles are read both as 16-byte rows (16 lanes:
+// 16 consecutive rows, one column) and through ds_read_b64_tr_b16 (32 lanes:
+// 4 consecutive rows x 64 bytes).  No padded stride serves both: the rows
+// need a stride of 4 dwords (odd multiple) modulo 64 banks, the transposing
+// reads 16 or 48.  Rows are therefore D + 32 elements apart (16 dwords
+// modulo 64) and the 16-byte chunk c of row r sits at chunk c ^ pair_swz(r):
+// 16 consecutive rows then cover 16 distinct 4-bank groups, and the 4 rows
+// of a transposing read keep their 64 bytes on distinct banks.  The swizzle
+// only permutes chunks within aligned groups of four, so column offsets of
+// 64 bytes and row offsets of 16 rows remain plain additions.
+__device__ __forceinline__ constexpr int pair_swz(int r) { return (r >> 2) & 3; }
+
 // Stages a [ROWS x D] bf16 tile: HBM -> registers (buffer loads, rows past the
 // end read as zero) -> row-major LDS.  Thread t holds rows (t + 256 r) / DCH,
 // 16-byte column t % DCH, r < CH.  The tile offset is a scalar, so the per-lane
@@ -63,9 +75,13 @@ struct TileStager {
     static_assert(CH * kBwdThreads == ROWS * DCH, "tile split");
     u32x4 reg[CH];
     int voff, lds_off;
-    __device__ TileStager(int tid, int stride) {
-        voff = ((tid / DCH) * D + 8 * (tid % DCH)) * 2;
-        lds_off = (tid / DCH) * stride + 8 * (tid % DCH);
+    // SWIZZLED: chunk c of row r is stored at chunk c ^ pair_swz(r) (the
+    // paired dK/dV kernel's layout; ROWS_PER_PASS is a multiple of 16, so the
+    // thread's rows all share one swizzle).
+    __device__ TileStager(int tid, int stride, bool swizzled = false) {
+        const int row = tid / DCH, c = tid % DCH;
+        voff = (row * D + 8 * c) * 2;
+        lds_off = row * stride + 8 * (swizzled ? c ^ pair_swz(row) : c);
     }
     __device__ void load(__amdgpu_buffer_rsrc_t rs, int row0) {
 #pragma unroll
@@ -425,7 +441,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
     const int G = GROUPED ? G_arg : 1;
     constexpr int BQ = kDkvBq;
     constexpr int NQH = BQ / 32;
-    constexpr int RS = both_ways_stride<D>();
+    constexpr int RS = D + 32;  // swizzled rows (pair_swz)
     constexpr bool FOLD = !DROPOUT;  // L and D ride in the products
     constexpr int NKS = D / 16 + (FOLD ? 1 : 0);  // k-steps of the S and dP chains
     static_assert(!FOLD || RS >= D + 16, "the folded k-step lives in the row padding");
@@ -492,10 +508,21 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
     const int nqblk = (N + BQ - 1) / BQ;
     const int iq0 = CAUSAL ? k0 / BQ : 0;
     const int iq_split = CAUSAL ? min(nqblk, (k0 + kFusedBkv - 1) / BQ + 1) : iq0;
-    TileStager<D, BQ> stq(tid, RS), stg(tid, RS);
+    TileStager<D, BQ> stq(tid, RS, true), stg(tid, RS, true);
     float lreg = 0.f, dreg = 0.f;
-    const int row_off = lq * RS + 8 * h;
-    const int tr_off = tr_row(lane) * RS + tr_col(lane);
+    // Row reads: k-step ks of row lq is logical chunk 2 ks + h, stored at
+    // 4 (ks / 2) + ((2 (ks % 2) + h) ^ pair_swz(lq)); one base per parity of ks.
+    const int row_off0 = lq * RS + 8 * (h ^ pair_swz(lq));
+    const int row_off1 = lq * RS + 8 * ((2 + h) ^ pair_swz(lq));
+    // Transposing reads: the lane's first row tr_row and second row tr_row + 8
+    // have their own swizzles.
+    const int trc = tr_col(lane);
+    const int tr_off0 = tr_row(lane) * RS + 8 * ((trc >> 3) ^ pair_swz(tr_row(lane))) + (trc & 7);
+    const int tr_off1 = (tr_row(lane) + 8) * RS + 8 * ((trc >> 3) ^ pair_swz(tr_row(lane) + 8)) + (trc & 7);
+    auto read_tr = [&](const bf16* p) __attribute__((always_inline)) {
+        const bf16x4 lo = lds_read_tr(p + tr_off0), hi = lds_read_tr(p + tr_off1);
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
 
     // Each role runs the loop as its own copy (DVW fixed at compile time), so
     // no role test branches inside a step and splits its scheduling regions;
@@ -524,8 +551,9 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                 if constexpr (FOLD) {
                     // Columns D .. D+7 of the row: the parts of -L/c and -D
                     // (lreg = +inf past N gives -inf: P = 0).
-                    *reinterpret_cast<u32x4*>(&sQ[buf][tid * RS + D]) = fold_parts(-lreg / scale_log2);
-                    *reinterpret_cast<u32x4*>(&sdO[buf][tid * RS + D]) = fold_parts(-dreg);
+                    const int fc = tid * RS + 8 * ((D / 8) ^ pair_swz(tid));
+                    *reinterpret_cast<u32x4*>(&sQ[buf][fc]) = fold_parts(-lreg / scale_log2);
+                    *reinterpret_cast<u32x4*>(&sdO[buf][fc]) = fold_parts(-dreg);
                 } else {
                     sL[buf][tid] = lreg;
                     sD[buf][tid] = dreg;
@@ -538,7 +566,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
             if (tid < 4 * BQ) {
                 const int t = tid % BQ, b = (tid / BQ) & 1;
                 bf16* dst = (tid / BQ) < 2 ? sQ[b] : sdO[b];
-                *reinterpret_cast<u32x4*>(&dst[t * RS + D + 8]) = u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4*>(&dst[t * RS + 8 * ((D / 8 + 1) ^ pair_swz(t))]) = u32x4{0u, 0u, 0u, 0u};
             }
         }
         if (iq0 < nqblk) {
@@ -559,12 +587,11 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
             for (int qh = 0; qh < NQH; ++qh) {
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
-                    acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(qsrc + 32 * qh * RS + tr_off + 32 * db, RS),
-                                                 dsk[2 * qh], acc[db]);
+                    acc[db] = mfma_bf16_32x32x16(read_tr(qsrc + 32 * qh * RS + 32 * db), dsk[2 * qh], acc[db]);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
-                    acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(qsrc + (32 * qh + 16) * RS + tr_off + 32 * db, RS),
-                                                 dsk[2 * qh + 1], acc[db]);
+                    acc[db] = mfma_bf16_32x32x16(read_tr(qsrc + (32 * qh + 16) * RS + 32 * db), dsk[2 * qh + 1],
+                                                 acc[db]);
             }
         };
         auto step = [&](int iq, auto mask_tag) __attribute__((always_inline)) {
@@ -584,7 +611,9 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                 const bf16* src = DVW ? qt : gt;
                 constexpr int NR = NQH * NKS, AHEAD = 4;
                 auto rread = [&](int r) {
-                    return lds_read16_early(src + 32 * (r % NQH) * RS + row_off + 16 * (r / NQH));
+                    const int ks = r / NQH;
+                    return lds_read16_early(src + 32 * (r % NQH) * RS + ((ks & 1) ? row_off1 : row_off0) +
+                                            32 * (ks >> 1));
                 };
                 bf16x8 ra[NR];
 #pragma unroll
@@ -700,13 +729,11 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                     for (int qh = 0; qh < NQH; ++qh) {
 #pragma unroll
                         for (int db = 0; db < D / 32; ++db)
-                            acc[db] = mfma_bf16_32x32x16(lds_read_tr_a(gt + 32 * qh * RS + tr_off + 32 * db, RS),
-                                                         bop[2 * qh], acc[db]);
+                            acc[db] = mfma_bf16_32x32x16(read_tr(gt + 32 * qh * RS + 32 * db), bop[2 * qh], acc[db]);
 #pragma unroll
                         for (int db = 0; db < D / 32; ++db)
-                            acc[db] = mfma_bf16_32x32x16(
-                                lds_read_tr_a(gt + (32 * qh + 16) * RS + tr_off + 32 * db, RS), bop[2 * qh + 1],
-                                acc[db]);
+                            acc[db] = mfma_bf16_32x32x16(read_tr(gt + (32 * qh + 16) * RS + 32 * db),
+                                                         bop[2 * qh + 1], acc[db]);
                     }
                 }
             }
