@@ -799,7 +799,10 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
     DropoutParams drop, int nx) {
     const float scale_log2 = ss.c;
     constexpr int BKV = kDqBkv;
-    constexpr int KS = both_ways_stride<D>();
+    // K is read both as rows and transposed: at d = 128 the swizzled layout of
+    // pair_swz, at d = 64 a padded stride that serves both.
+    constexpr bool SWZ = D == 128;
+    constexpr int KS = SWZ ? D + 32 : both_ways_stride<D>();
     constexpr int VS = D + 8;  // rows only
     __shared__ __attribute__((aligned(16))) bf16 sK[2][BKV * KS];
     __shared__ __attribute__((aligned(16))) bf16 sV[2][BKV * VS];
@@ -845,10 +848,17 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
 
     int ntiles = (N + BKV - 1) / BKV;
     if (CAUSAL) ntiles = min(ntiles, (min(q0 + kDqBq, N) - 1) / BKV + 1);
-    TileStager<D, BKV> stk(tid, KS), stv(tid, VS);
-    const int k_off = lq * KS + 8 * h;
+    TileStager<D, BKV> stk(tid, KS, SWZ), stv(tid, VS);
+    // K row reads: k-step ks of row lq is logical chunk 2 ks + h (swizzled:
+    // one base per parity of ks); transposing reads of K^T: one base per row
+    // of the lane (tr_row, tr_row + 8).
+    const int k_off0 = lq * KS + 8 * (SWZ ? h ^ pair_swz(lq) : h);
+    const int k_off1 = SWZ ? lq * KS + 8 * ((2 + h) ^ pair_swz(lq)) : k_off0 + 16;
     const int v_off = lq * VS + 8 * h;
-    const int tr_off = tr_row(lane) * KS + tr_col(lane);
+    const int trc = tr_col(lane);
+    const int tr_off0 = tr_row(lane) * KS + (SWZ ? 8 * ((trc >> 3) ^ pair_swz(tr_row(lane))) + (trc & 7) : trc);
+    const int tr_off1 = (tr_row(lane) + 8) * KS +
+                        (SWZ ? 8 * ((trc >> 3) ^ pair_swz(tr_row(lane) + 8)) + (trc & 7) : trc);
 
     stk.load(krs, 0);
     stv.load(vrs, 0);
@@ -888,8 +898,10 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
                 // MFMAs (non-causal N18000 4% slower, causal within 1%).
                 constexpr int NR = 2 * (D / 16), AHEAD = 4;
                 auto rread = [&](int r) {
-                    return (r & 1) ? lds_read16_early(vt + 32 * kh * VS + v_off + 16 * (r >> 1))
-                                   : lds_read16_early(kt + 32 * kh * KS + k_off + 16 * (r >> 1));
+                    const int ks = r >> 1;
+                    return (r & 1) ? lds_read16_early(vt + 32 * kh * VS + v_off + 16 * ks)
+                                   : lds_read16_early(kt + 32 * kh * KS + ((ks & 1) ? k_off1 : k_off0) +
+                                                      32 * (ks >> 1));
                 };
                 bf16x8 ra[NR];
 #pragma unroll
@@ -923,8 +935,12 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
             for (int s2 = 0; s2 < BKV / 16; ++s2)
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
-                    dqacc[db] = mfma_bf16_32x32x16(lds_read_tr_a(kt + 16 * s2 * KS + tr_off + 32 * db, KS), dsf[s2],
-                                                   dqacc[db]);
+                {
+                    const bf16* p = kt + 16 * s2 * KS + 32 * db;
+                    const bf16x4 lo = lds_read_tr(p + tr_off0), hi = lds_read_tr(p + tr_off1);
+                    dqacc[db] = mfma_bf16_32x32x16(bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]},
+                                                   dsf[s2], dqacc[db]);
+                }
         }
         stk.store(sK[buf ^ 1], KS);
         stv.store(sV[buf ^ 1], VS);
