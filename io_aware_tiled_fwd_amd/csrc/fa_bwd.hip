@@ -63,6 +63,23 @@ constexpr int both_ways_stride() { return D == 128 ? D + 24 : D + 8; }
 // 64 bytes and row offsets of 16 rows remain plain additions.
 __device__ __forceinline__ constexpr int pair_swz(int r) { return (r >> 2) & 3; }
 
+// Pins the issue order of a chain of N MFMAs whose A operands come from LDS in
+// R reads each: the reads of the first A MFMAs, then every MFMA followed by
+// the reads of the MFMA A places on.  Without it the compiler issued each read
+// right before its MFMA and waited for it there (one LDS round trip per MFMA),
+// whatever order the source gave.  Applies to the basic block it sits in.
+template <int N, int R, int A>
+__device__ __forceinline__ void pin_read_ahead() {
+    static_assert(A <= N, "read-ahead longer than the chain");
+    __builtin_amdgcn_sched_group_barrier(0x100, R * A, 0);
+#pragma unroll
+    for (int i = 0; i < N - A; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
+}
+
 // Stages a [ROWS x D] bf16 tile: HBM -> registers (buffer loads, rows past the
 // end read as zero) -> row-major LDS.  Thread t holds rows (t + 256 r) / DCH,
 // 16-byte column t % DCH, r < CH.  The tile offset is a scalar, so the per-lane
@@ -413,6 +430,12 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
 //    is dropped, and the dK wavefront needs no generator of its own.  (At
 //    d = 64 the separate kernels are faster and are used instead.)
 constexpr int kPairs = kBwdWaves / 2;
+// MFMAs of read-ahead for the transposing-read operands of the dV and dK
+// products.
+#ifndef FA_TR_AHEAD
+#define FA_TR_AHEAD 3
+#endif
+constexpr int kTrAhead = FA_TR_AHEAD;
 constexpr int kFusedBkv = 32 * kPairs;  // keys per workgroup
 
 // x as hi + mid + lo, three bf16 values whose sum is x exactly (x finite:
@@ -593,6 +616,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                     acc[db] = mfma_bf16_32x32x16(read_tr(qsrc + (32 * qh + 16) * RS + 32 * db), dsk[2 * qh + 1],
                                                  acc[db]);
             }
+            pin_read_ahead<2 * NQH * (D / 32), 2, kTrAhead>();
         };
         auto step = [&](int iq, auto mask_tag) __attribute__((always_inline)) {
             constexpr bool MASK = decltype(mask_tag)::value;
@@ -625,6 +649,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                     if (r + AHEAD < NR) ra[r + AHEAD] = rread(r + AHEAD);
                     t[r % NQH] = mfma_bf16_32x32x16(ra[r], kvf[r / NQH], t[r % NQH]);
                 }
+                pin_read_ahead<NR, 1, AHEAD>();
                 // The dK wavefront forms dP - D while its partner computes P,
                 // leaving one product per element for phase 2 (with FOLD the
                 // chain has formed it).
@@ -735,6 +760,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                             acc[db] = mfma_bf16_32x32x16(read_tr(gt + (32 * qh + 16) * RS + 32 * db),
                                                          bop[2 * qh + 1], acc[db]);
                     }
+                    pin_read_ahead<2 * NQH * (D / 32), 2, kTrAhead>();
                 }
             }
             if constexpr (!DVW) {
