@@ -532,6 +532,13 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
     const int iq0 = CAUSAL ? k0 / BQ : 0;
     const int iq_split = CAUSAL ? min(nqblk, (k0 + kFusedBkv - 1) / BQ + 1) : iq0;
     TileStager<D, BQ> stq(tid, RS, true), stg(tid, RS, true);
+    // L and D of the staged block's rows travel through the first wavefront's
+    // lanes.  L is kept as loaded until the block is stored: scaling it at load
+    // time made that wavefront wait for the load, and with it for the tile
+    // loads issued before it, at the start of every step (carrying them on
+    // lanes of the dK wavefronts instead measured slower).
+    const bool stat_lane = tid < BQ;
+    const int srow = tid;
     float lreg = 0.f, dreg = 0.f;
     // Row reads: k-step ks of row lq is logical chunk 2 ks + h, stored at
     // 4 (ks / 2) + ((2 (ks % 2) + h) ^ pair_swz(lq)); one base per parity of ks.
@@ -561,25 +568,26 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
             const int i0 = iq * BQ;
             stq.load(qrs, i0);
             stg.load(grs, i0);
-            if (tid < BQ) {
-                const int r = min(i0 + tid, N - 1);
-                lreg = i0 + tid < N ? lse_h[r] * kLog2e : INFINITY;
-                dreg = i0 + tid < N ? d_h[r] : 0.f;
+            if (stat_lane) {
+                const int r = min(i0 + srow, N - 1);
+                lreg = i0 + srow < N ? lse_h[r] : INFINITY;
+                dreg = i0 + srow < N ? d_h[r] : 0.f;
             }
         };
         auto store_block = [&](int buf) {
             stq.store(sQ[buf], RS);
             stg.store(sdO[buf], RS);
-            if (tid < BQ) {
+            if (stat_lane) {
+                const float l2 = lreg * kLog2e;  // log2 domain; +inf past N
                 if constexpr (FOLD) {
                     // Columns D .. D+7 of the row: the parts of -L/c and -D
-                    // (lreg = +inf past N gives -inf: P = 0).
-                    const int fc = tid * RS + 8 * ((D / 8) ^ pair_swz(tid));
-                    *reinterpret_cast<u32x4*>(&sQ[buf][fc]) = fold_parts(-lreg / scale_log2);
+                    // (l2 = +inf past N gives -inf: P = 0).
+                    const int fc = srow * RS + 8 * ((D / 8) ^ pair_swz(srow));
+                    *reinterpret_cast<u32x4*>(&sQ[buf][fc]) = fold_parts(-l2 / scale_log2);
                     *reinterpret_cast<u32x4*>(&sdO[buf][fc]) = fold_parts(-dreg);
                 } else {
-                    sL[buf][tid] = lreg;
-                    sD[buf][tid] = dreg;
+                    sL[buf][srow] = l2;
+                    sD[buf][srow] = dreg;
                 }
             }
         };
