@@ -249,7 +249,9 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
             stg.load(grs, i0);
             if (tid < BQ) {
                 const int r = min(i0 + tid, N - 1);
-                lreg = i0 + tid < N ? lse_h[r] * kLog2e : INFINITY;  // P = 0 past N
+                // Kept as loaded until the block is stored (scaling it here
+                // would wait for the load at the start of the step).
+                lreg = i0 + tid < N ? lse_h[r] : INFINITY;  // P = 0 past N
                 if constexpr (DK) dreg = i0 + tid < N ? d_h[r] : 0.f;
             }
         };
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_kernel(
             stq.store(sQ[buf], RS);
             stg.store(sdO[buf], RS);
             if (tid < BQ) {
-                sL[buf][tid] = lreg;
+                sL[buf][tid] = lreg * kLog2e;
                 if constexpr (DK) sD[buf][tid] = dreg;
             }
         };
