@@ -45,9 +45,11 @@ constexpr int kBwdWaves = FA_BWD_WAVES;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 
 // Row stride (elements) of a bf16 [rows][D] LDS tile that is read both as
-// 16-byte rows (MFMA operand M) and through ds_read_b64_tr_b16 (operand M^T):
-// 16 consecutive rows of one 16-byte column, and 4 consecutive rows of 32
-// bytes, each fall on distinct banks (measured on gfx950).
+// 16-byte rows (MFMA operand M) and through ds_read_b64_tr_b16 (operand M^T),
+// in the separate dK/dV kernels: 16 consecutive rows of one 16-byte column
+// fall on distinct banks.  At d = 128 the transposing reads of this stride
+// still meet 2-way conflicts; the paired dK/dV and the dQ kernels use the
+// swizzled layout of pair_swz (below) instead.
 template <int D>
 constexpr int both_ways_stride() { return D == 128 ? D + 24 : D + 8; }
 
