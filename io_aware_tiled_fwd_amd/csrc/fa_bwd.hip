@@ -543,6 +543,10 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
     // lanes of the dK wavefronts instead measured slower).
     const bool stat_lane = tid < BQ;
     const int srow = tid;
+    // -L/c as -L2 times 1/c, formed once: a division per step sat on the
+    // first wavefront's path to the step's end barrier.  (Only the sum of the
+    // three parts matters, and c (S - L2/c) meets L2 to within rounding.)
+    const float inv_c = 1.f / scale_log2;
     float lreg = 0.f, dreg = 0.f;
     // Row reads: k-step ks of row lq is logical chunk 2 ks + h, stored at
     // 4 (ks / 2) + ((2 (ks % 2) + h) ^ pair_swz(lq)); one base per parity of ks.
@@ -587,7 +591,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
                     // Columns D .. D+7 of the row: the parts of -L/c and -D
                     // (l2 = +inf past N gives -inf: P = 0).
                     const int fc = srow * RS + 8 * ((D / 8) ^ pair_swz(srow));
-                    *reinterpret_cast<u32x4*>(&sQ[buf][fc]) = fold_parts(-l2 / scale_log2);
+                    *reinterpret_cast<u32x4*>(&sQ[buf][fc]) = fold_parts(-l2 * inv_c);
                     *reinterpret_cast<u32x4*>(&sdO[buf][fc]) = fold_parts(-dreg);
                 } else {
                     sL[buf][srow] = l2;
