@@ -127,3 +127,38 @@ def test_hot_kernels_do_not_spill(code_objects):
         assert hits, f"kernel {frag} not found in the code objects"
         for n, c in hits.items():
             assert c == 0, f"{n} spills {c} VGPRs"
+
+
+# Kernels whose MFMA chains must keep their LDS operand reads ahead of them
+# (pin_read_ahead in fa_bwd.hip), and the largest fraction of their MFMAs
+# that may sit right behind an s_waitcnt lgkmcnt(0).  Without the pinned
+# order the compiler issued each read just before its MFMA and waited for it
+# there: 44% of the paired kernel's MFMAs and 36% of the causal dQ kernel's,
+# against under 7% with it.
+READ_AHEAD = {
+    "bwd_dkdv_fused_kernelILi128ELb1ELb0ELb0EfE": 0.10, "bwd_dkdv_fused_kernelILi128ELb0ELb0ELb0EfE": 0.10,
+    "bwd_dq_kernelILi128ELb1ELb0EfE": 0.10,
+}
+
+
+def test_backward_chains_read_ahead(code_objects):
+    counts = {}
+    for co in code_objects:
+        dis = subprocess.run([TOOLS["llvm-objdump"], "-d", str(co)], capture_output=True, text=True, check=True).stdout
+        cur, prev = None, ""
+        for line in dis.splitlines():
+            m = re.match(r"^[0-9a-f]+ <(\S+)>:", line)
+            if m:
+                cur, prev = m.group(1), ""
+                continue
+            frag = next((f for f in READ_AHEAD if cur and f in cur), None)
+            ins = line.strip()
+            if frag is None or not ins:
+                continue
+            if ins.startswith("v_mfma"):
+                total, waited = counts.get(frag, (0, 0))
+                counts[frag] = (total + 1, waited + (prev.startswith("s_waitcnt") and "lgkmcnt(0)" in prev))
+            prev = ins
+    assert set(counts) == set(READ_AHEAD), f"kernels not found: {set(READ_AHEAD) - set(counts)}"
+    for frag, (total, waited) in counts.items():
+        assert waited <= READ_AHEAD[frag] * total, f"{frag}: {waited} of {total} MFMAs right after lgkmcnt(0)"
