@@ -53,9 +53,10 @@ constexpr int kBwdThreads = 64 * kBwdWaves;
 template <int D>
 constexpr int both_ways_stride() { return D == 128 ? D + 24 : D + 8; }
 
-// The paired dK/dV kernel's tiles are read both as 16-byte rows (16 lanes:
-// 16 consecutive rows, one column) and through ds_read_b64_tr_b16 (32 lanes:
-// 4 consecutive rows x 64 bytes).  No padded stride serves both: the rows
+// The tiles that the paired dK/dV kernel (Q, dO) and the dQ kernel (K) read
+// both as 16-byte rows (16 lanes: 16 consecutive rows, one column) and
+// through ds_read_b64_tr_b16 (32 lanes: 4 consecutive rows x 64 bytes), at
+// d = 128.  No padded stride serves both: the rows
 // need a stride of 4 dwords (odd multiple) modulo 64 banks, the transposing
 // reads 16 or 48.  Rows are therefore D + 32 elements apart (16 dwords
 // modulo 64) and the 16-byte chunk c of row r sits at chunk c ^ pair_swz(r):
@@ -95,7 +96,7 @@ struct TileStager {
     u32x4 reg[CH];
     int voff, lds_off;
     // SWIZZLED: chunk c of row r is stored at chunk c ^ pair_swz(r) (the
-    // paired dK/dV kernel's layout; ROWS_PER_PASS is a multiple of 16, so the
+    // both-ways layout above; ROWS_PER_PASS is a multiple of 16, so the
     // thread's rows all share one swizzle).
     __device__ TileStager(int tid, int stride, bool swizzled = false) {
         const int row = tid / DCH, c = tid % DCH;
@@ -537,15 +538,15 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
     const int iq_split = CAUSAL ? min(nqblk, (k0 + kFusedBkv - 1) / BQ + 1) : iq0;
     TileStager<D, BQ> stq(tid, RS, true), stg(tid, RS, true);
     // L and D of the staged block's rows travel through the first wavefront's
-    // lanes.  L is kept as loaded until the block is stored: scaling it at load
-    // time made that wavefront wait for the load, and with it for the tile
-    // loads issued before it, at the start of every step (carrying them on
-    // lanes of the dK wavefronts instead measured slower).
-    const bool stat_lane = tid < BQ;
-    const int srow = tid;
-    // -L/c as -L2 times 1/c, formed once: a division per step sat on the
-    // first wavefront's path to the step's end barrier.  (Only the sum of the
-    // three parts matters, and c (S - L2/c) meets L2 to within rounding.)
+    // lanes (thread t: row t).  L is kept as loaded until the block is stored:
+    // scaling it at load time made that wavefront wait for the load, and with
+    // it for the tile loads issued before it, at the start of every step
+    // (carrying the rows on lanes of the dK wavefronts instead measured
+    // slower).
+    // -L/c is formed as -L2 times 1/c, the reciprocal taken once: a division
+    // per step sat on the first wavefront's path to the step's end barrier.
+    // Only the sum of the three parts matters, and c (S - L2 (1/c)) equals
+    // c S - L2 to within rounding.
     const float inv_c = 1.f / scale_log2;
     float lreg = 0.f, dreg = 0.f;
     // Row reads: k-step ks of row lq is logical chunk 2 ks + h, stored at
@@ -576,26 +577,26 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
             const int i0 = iq * BQ;
             stq.load(qrs, i0);
             stg.load(grs, i0);
-            if (stat_lane) {
-                const int r = min(i0 + srow, N - 1);
-                lreg = i0 + srow < N ? lse_h[r] : INFINITY;
-                dreg = i0 + srow < N ? d_h[r] : 0.f;
+            if (tid < BQ) {
+                const int r = min(i0 + tid, N - 1);
+                lreg = i0 + tid < N ? lse_h[r] : INFINITY;
+                dreg = i0 + tid < N ? d_h[r] : 0.f;
             }
         };
         auto store_block = [&](int buf) {
             stq.store(sQ[buf], RS);
             stg.store(sdO[buf], RS);
-            if (stat_lane) {
+            if (tid < BQ) {
                 const float l2 = lreg * kLog2e;  // log2 domain; +inf past N
                 if constexpr (FOLD) {
                     // Columns D .. D+7 of the row: the parts of -L/c and -D
                     // (l2 = +inf past N gives -inf: P = 0).
-                    const int fc = srow * RS + 8 * ((D / 8) ^ pair_swz(srow));
+                    const int fc = tid * RS + 8 * ((D / 8) ^ pair_swz(tid));
                     *reinterpret_cast<u32x4*>(&sQ[buf][fc]) = fold_parts(-l2 * inv_c);
                     *reinterpret_cast<u32x4*>(&sdO[buf][fc]) = fold_parts(-dreg);
                 } else {
-                    sL[buf][srow] = l2;
-                    sD[buf][srow] = dreg;
+                    sL[buf][tid] = l2;
+                    sD[buf][tid] = dreg;
                 }
             }
         };
