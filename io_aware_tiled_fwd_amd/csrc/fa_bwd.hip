@@ -959,9 +959,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
                     if (r & 1) dp = mfma_bf16_32x32x16(ra[r], gf[r >> 1], dp);
                     else s = mfma_bf16_32x32x16(ra[r], qf[r >> 1], s);
                 }
-#ifndef FA_DQ_NOPIN
                 pin_read_ahead<NR, 1, AHEAD>();
-#endif
                 float v[16];
                 u32x4 dw;
                 if constexpr (DROPOUT) dw = dropout_words(drop, bh, qrow, k0 / 32 + kh, h);
@@ -991,9 +989,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
                     dqacc[db] = mfma_bf16_32x32x16(bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]},
                                                    dsf[s2], dqacc[db]);
                 }
-#ifndef FA_DQ_NOPIN
             pin_read_ahead<(BKV / 16) * (D / 32), 2, kTrAhead>();
-#endif
         }
         stk.store(sK[buf ^ 1], KS);
         stv.store(sV[buf ^ 1], VS);
