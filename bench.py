@@ -120,11 +120,11 @@ def timed_rounds(calls, iters, rounds=3, gap_s=0.05):
     """Per-iteration HIP-event times of `calls` (a list of callables run in
     order each iteration, each timed separately) over `rounds` rounds of
     `iters` iterations, a short pause between rounds.  Returns (the per-call
-    medians of the round whose summed median is lowest, every round's medians).
+    medians of the middle round by summed median, every round's medians).
     On some boxes one stretch of a run occasionally went about 2.4x slower
-    throughout while a standalone timing was normal; the best round and the
-    list of all rounds keep such a stretch visible without letting it set the
-    figure."""
+    throughout while a standalone timing was normal; the middle of three
+    rounds keeps one such stretch, or one unusually fast round, from setting
+    the figure, and the list of all rounds keeps it visible."""
     import time
 
     import numpy as np
@@ -144,8 +144,8 @@ def timed_rounds(calls, iters, rounds=3, gap_s=0.05):
                 e[j + 1].record(stream)
         torch.cuda.synchronize()
         per_round.append([float(np.median([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(len(calls))])
-    best = min(per_round, key=sum)
-    return best, per_round
+    mid = sorted(per_round, key=sum)[len(per_round) // 2]
+    return mid, per_round
 
 
 def fp8_leg(t, B, H, N, d, causal, scale, iters=10, warmup=3):
@@ -216,7 +216,7 @@ def dropout_leg(t, B, H, N, d, causal, scale, p=0.1, iters=5, warmup=2):
 def decode_leg(name, iters=20, warmup=5):
     """Time fa_decode (split kernel + merge kernel) with HIP events on the
     launch stream; rate = compulsory bytes (K, V, q, o, L once) / median time
-    (best of three rounds, see timed_rounds)."""
+    (the middle of three rounds, see timed_rounds)."""
     import numpy as np
     import torch
 
