@@ -824,16 +824,20 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dkdv_fused_ker
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ.  Per tile of 64 keys, staged row-major in LDS (double buffered): K
+// 3. dQ.  Per tile of keys (kDqBkv), staged row-major in LDS (double buffered): K
 //    (read both as rows and transposed) and V (rows).
-//    Per wavefront (32 queries) and 32-key half, with C tiles [key x query]:
+//    Per wavefront (32 queries) and 32-key part of the tile, with C tiles [key x query]:
 //      S^T  = K Q^T      (A = K rows from LDS, B = Q^T from registers)
 //      dP^T = V dO^T     (A = V rows from LDS, B = dO^T from registers)
 //      P^T = exp2(S^T c - L2), dS^T = P^T (dP^T - D)
 //      dQ^T += K^T dS^T  (A = K^T: transposing LDS reads; B = dS^T from registers)
 
 constexpr int kDqBq = 32 * kBwdWaves;  // query rows per workgroup
-constexpr int kDqBkv = 64;  // keys per step
+// Keys per step: 128 at d = 64 (fewer barriers and staging rounds per key),
+// 64 at d = 128, where the dS operands of 128 keys, live until the step's dQ
+// products, no longer fit in the registers.
+template <int D>
+constexpr int kDqBkv = D == 64 ? 128 : 64;
 
 // DROPOUT: dS = P (z dP - D) with z the forward's dropout factor (0 or the
 // keep scale); a lane holds a query row and 16 keys per C tile, the layout
@@ -845,7 +849,7 @@ __global__ __launch_bounds__(kBwdThreads, 8 / kBwdWaves) void bwd_dq_kernel(
     OutT* __restrict__ dQ, int N, int BH, int nqb, ScoreScale ss, float scale, int Hq, int G,
     DropoutParams drop, int nx) {
     const float scale_log2 = ss.c;
-    constexpr int BKV = kDqBkv;
+    constexpr int BKV = kDqBkv<D>;
     // K is read both as rows and transposed: at d = 128 the swizzled layout of
     // pair_swz, at d = 64 a padded stride that serves both.
     constexpr bool SWZ = D == 128;
